@@ -1,0 +1,208 @@
+"""Seeded synthetic inputs for KDA prefill and decode.
+
+Shared by the tests, the smoke check and the bench.  This module only draws
+random inputs of the right shapes and value distributions; it holds none of
+the method's arithmetic.  Everything is generated on the CPU with a seeded
+``torch.Generator``, so the GPU path and the CPU oracle receive exactly the
+same numbers (the caller copies them to the device).
+
+Value recipes (the pool-mode test of sglang PR 30169's digest fixes the style:
+q, k normalised in fp32 then cast, beta = sigmoid(N(0,1)), initial states
+0.05 * N(0,1), random slots in a larger pool):
+
+* q, k ~ N(0,1), L2-normalised over K in fp32, then cast to the io dtype.
+* v ~ N(0,1) in the io dtype.
+* beta = sigmoid(N(0,1)), fp32.
+* per-channel log-gate  g = -exp(a_c) * softplus(x + dt_bias_c), with a_c and
+  dt_bias_c fixed per (value head, channel) and x ~ N(0,1) per
+  (token, value head, channel).  "moderate" gates: a_c ~ U(-1, 1),
+  dt_bias_c = 0.  "realistic" gates: a_c ~ U(-1, 2.7),
+  dt_c = exp(U(ln 1e-3, ln 64)), dt_bias_c = dt_c + ln(-expm1(-dt_c)) (the
+  inverse softplus of dt_c), which drives in-chunk cumulative log-decays to
+  the 1e3..6e4 range.
+* scalar (GDN) gates: the same recipe with one value per (token, value head).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _gen(seed: int) -> torch.Generator:
+    return torch.Generator().manual_seed(int(seed))
+
+
+def unit_rows(gen, shape, dtype):
+    """N(0,1) rows L2-normalised over the last axis in fp32, then cast."""
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    x = x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+    return x.to(dtype)
+
+
+def gate_params(gen, hv, dk, kind):
+    """Per-(value head, channel) gate parameters (a_c, dt_bias_c)."""
+    if kind == "moderate":
+        a = torch.rand(hv, dk, generator=gen) * 2.0 - 1.0
+        dt_bias = torch.zeros(hv, dk)
+    elif kind == "realistic":
+        a = torch.rand(hv, dk, generator=gen) * 3.7 - 1.0
+        lo, hi = math.log(1e-3), math.log(64.0)
+        dt = torch.exp(torch.rand(hv, dk, generator=gen, dtype=torch.float64) * (hi - lo) + lo)
+        dt_bias = (dt + torch.log(-torch.expm1(-dt))).float()
+    else:
+        raise ValueError(kind)
+    return a, dt_bias
+
+
+def log_gates(gen, T, hv, dk, kind="moderate", scalar=False):
+    """g <= 0: [T, hv, dk] per channel, or [T, hv] for the scalar gate."""
+    width = 1 if scalar else dk
+    a, dt_bias = gate_params(gen, hv, width, kind)
+    x = torch.randn(T, hv, width, generator=gen)
+    g = -torch.exp(a)[None] * torch.nn.functional.softplus(x + dt_bias[None])
+    return g[..., 0].contiguous() if scalar else g.contiguous()
+
+
+def seq_lengths(gen, n, lo, hi):
+    """n lengths uniform on the integers lo..hi inclusive."""
+    return torch.randint(lo, hi + 1, (n,), generator=gen, dtype=torch.int32)
+
+
+def cu_from_lengths(lengths):
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.as_tensor(lengths, dtype=torch.int32).cumsum(0)
+    return cu
+
+
+@dataclass
+class Prefill:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    cu_seqlens: torch.Tensor
+    h0: Optional[torch.Tensor] = None          # dense [N, Hv, V, K]
+    pool: Optional[torch.Tensor] = None        # [S, Hv, V, K]
+    indices: Optional[torch.Tensor] = None     # [N] int32, -1 = padding
+    scale: float = 1.0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self):
+        return self.cu_seqlens.numel() - 1
+
+
+def make_prefill(seed, lengths, hk, hv, dk, dv, io="bf16", gate="moderate",
+                 scalar_gate=False, h0=None, pool_slots=0, state_dtype="f32",
+                 pad_one=False, scale=1.0):
+    """Generic seeded prefill input.  ``lengths`` is a list of ints, or a tuple
+    (n, lo, hi) for n lengths drawn uniformly from lo..hi.  ``h0`` is None
+    (zeros), "random" (0.05*N(0,1)).  ``pool_slots`` > 0 builds a pool of that
+    many random rows and per-sequence slot indices drawn without replacement
+    from [0, pool_slots - 1); with ``pad_one`` the last index is -1."""
+    gen = _gen(seed)
+    dt = DTYPES[io]
+    if isinstance(lengths, tuple):
+        n, lo, hi = lengths
+        lens = seq_lengths(gen, n, lo, hi)
+    else:
+        lens = torch.as_tensor(lengths, dtype=torch.int32)
+    cu = cu_from_lengths(lens)
+    T = int(cu[-1])
+    n = len(lens)
+    q = unit_rows(gen, (T, hk, dk), dt)
+    k = unit_rows(gen, (T, hk, dk), dt)
+    v = torch.randn(T, hv, dv, generator=gen).to(dt)
+    beta = torch.sigmoid(torch.randn(T, hv, generator=gen))
+    g = log_gates(gen, T, hv, dk, gate, scalar_gate)
+    sd = DTYPES[state_dtype]
+    inp = Prefill(q, k, v, g, beta, cu, scale=scale,
+                  meta=dict(seed=seed, hk=hk, hv=hv, dk=dk, dv=dv, io=io, gate=gate,
+                            scalar_gate=scalar_gate, state_dtype=state_dtype, T=T))
+    if h0 == "random":
+        inp.h0 = (torch.randn(n, hv, dv, dk, generator=gen) * 0.05).to(sd)
+    if pool_slots:
+        inp.pool = (torch.randn(pool_slots, hv, dv, dk, generator=gen) * 0.05).to(sd)
+        idx = torch.randperm(pool_slots - 1, generator=gen)[:n].to(torch.int32)
+        if pad_one:
+            idx[-1] = -1
+        inp.indices = idx
+    return inp
+
+
+def config1(seed=1):
+    """One sequence of 128 tokens (two chunks), Hk=Hv=1, K=V=32, fp32 io,
+    moderate per-channel gates, zero initial state."""
+    return make_prefill(seed, [128], 1, 1, 32, 32, io="f32")
+
+
+def config2(seed=2):
+    """Five sequences, lengths U{1..130}, Hk=4, Hv=8, K=V=128, bf16 io,
+    moderate gates, random fp32 initial states."""
+    return make_prefill(seed, (5, 1, 130), 4, 8, 128, 128, h0="random")
+
+
+def config3(seed=11, state_dtype="f32"):
+    """Config 2's shapes in pool mode: 64-slot pool, slots drawn without
+    replacement from [0, 63), the last sequence's index set to -1 (sentinel
+    slot 63)."""
+    return make_prefill(seed, (5, 1, 130), 4, 8, 128, 128, pool_slots=64,
+                        state_dtype=state_dtype, pad_one=True)
+
+
+def config4(seed=4):
+    """Kimi-Linear-shaped prefill: 16 sequences, lengths U{512..4096},
+    Hk=Hv=32, K=V=128, bf16 io, realistic gates, fp32 pool of 32 slots."""
+    return make_prefill(seed, (16, 512, 4096), 32, 32, 128, 128, gate="realistic",
+                        pool_slots=32)
+
+
+@dataclass
+class Decode:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    pool: torch.Tensor
+    indices: torch.Tensor
+    scale: float = 1.0
+    meta: dict = field(default_factory=dict)
+
+
+def make_decode(seed, batch, hk, hv, dk, dv, num_slots, io="bf16", gate="realistic",
+                scalar_gate=False, state_dtype="f32", pad=0, scale=1.0):
+    """``batch`` one-token requests over a pool of ``num_slots`` rows; slot
+    indices are a random permutation of [0, num_slots - 1) cut to ``batch``
+    (the sentinel slot num_slots-1 is never drawn); the last ``pad`` indices
+    are set to -1."""
+    gen = _gen(seed)
+    dt = DTYPES[io]
+    q = unit_rows(gen, (batch, hk, dk), dt)
+    k = unit_rows(gen, (batch, hk, dk), dt)
+    v = torch.randn(batch, hv, dv, generator=gen).to(dt)
+    beta = torch.sigmoid(torch.randn(batch, hv, generator=gen))
+    g = log_gates(gen, batch, hv, dk, gate, scalar_gate)
+    assert batch <= num_slots - 1
+    idx = torch.randperm(num_slots - 1, generator=gen)[:batch].to(torch.int32)
+    if pad:
+        idx[batch - pad:] = -1
+    pool = torch.empty(num_slots, hv, dv, dk, dtype=DTYPES[state_dtype])
+    # draw the pool row by row so a 8.7 GB pool never needs a second fp32 copy
+    for s in range(num_slots):
+        pool[s] = torch.randn(hv, dv, dk, generator=gen) * 0.05
+    return Decode(q, k, v, g, beta, pool, idx, scale,
+                  meta=dict(seed=seed, batch=batch, hk=hk, hv=hv, dk=dk, dv=dv, io=io,
+                            state_dtype=state_dtype, num_slots=num_slots))
+
+
+def config5(seed=5, batch=4096, num_slots=4160):
+    """Recurrent decode: 4096 one-token requests, Hk=Hv=32, K=V=128, bf16 io,
+    realistic gates, fp32 pool of 4160 slots."""
+    return make_decode(seed, batch, 32, 32, 128, 128, num_slots)
