@@ -1,0 +1,193 @@
+"""Python binding of libkda (KDA gated delta rule on MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libkda.so``.  PyTorch supplies device memory and the current
+stream.  The library must have been built (``python -m
+gated_delta_rule_51_amd.build``); importing the binding never falls back to
+anything else.
+
+    o, final_state = chunk_prefill(q, k, v, g, beta, cu_seqlens,
+                                   initial_state=None, state_indices=None,
+                                   scale=1.0, output_final_state=True)
+    o = recurrent_decode(q, k, v, g, beta, state_pool, state_indices, scale=1.0)
+
+Layouts (contiguous): q, k [T, Hk, K]; v [T, Hv, V]; g [T, Hv, K] (per-channel
+gate) or [T, Hv] (scalar gate); beta [T, Hv] fp32; states [.., Hv, V, K].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["chunk_prefill", "recurrent_decode", "workspace_size", "library_path", "KdaError"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+F32, BF16 = 0, 1
+GATE_CHANNEL, GATE_SCALAR = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class KdaError(RuntimeError):
+    pass
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("hk", ctypes.c_int32), ("hv", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("num_slots", ctypes.c_int32)]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("hk", ctypes.c_int32), ("hv", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("num_slots", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libkda (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise KdaError("libkda.so is not built; run `python -m gated_delta_rule_51_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
+        L.kda_chunk_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc)]
+        L.kda_chunk_prefill.restype = ctypes.c_int
+        L.kda_chunk_prefill.argtypes = [ctypes.POINTER(PrefillDesc)] + [_P] * 11 + [ctypes.c_size_t, _P]
+        L.kda_recurrent_decode.restype = ctypes.c_int
+        L.kda_recurrent_decode.argtypes = [ctypes.POINTER(DecodeDesc)] + [_P] * 9
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise KdaError("libkda: %s (status %d)" % (lib().kda_status_string(status).decode(), status))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype=None, ndim=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims" % (name, ndim))
+
+
+def _io_dtype(q):
+    if q.dtype not in _DT:
+        raise ValueError("q/k/v must be float32 or bfloat16")
+    return _DT[q.dtype]
+
+
+def prefill_desc(q, v, g, num_seqs, state_dtype, scale, num_slots=0):
+    T, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    return PrefillDesc(num_seqs, T, hk, hv, dk, dv, _io_dtype(q), _DT[state_dtype],
+                       GATE_SCALAR if g.dim() == 2 else GATE_CHANNEL, float(scale), num_slots)
+
+
+def workspace_size(desc: PrefillDesc) -> int:
+    return int(lib().kda_chunk_prefill_workspace_size(ctypes.byref(desc)))
+
+
+# One workspace per (device, stream); calls ordered on one stream may share it.
+_WS = {}
+
+
+def _workspace(device, stream, nbytes):
+    key = (device.index, stream)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_indices=None,
+                  scale=1.0, output_final_state=True, state_dtype=None):
+    """Chunked prefill over packed sequences.  Returns (o, final_state).
+
+    Dense mode (state_indices is None): initial_state [N, Hv, V, K] or None
+    (zeros); final_state is a new [N, Hv, V, K] tensor (or None when
+    output_final_state is False).  Pool mode: initial_state is the pool
+    [slots, Hv, V, K], updated in place at state_indices (negative -> last
+    slot), and returned as final_state."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, 3)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32, 2)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(initial_state, "initial_state", None, 4)
+    _need(state_indices, "state_indices", torch.int32, 1)
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    T, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    pool = state_indices is not None
+    sd = initial_state.dtype if initial_state is not None else (state_dtype or torch.float32)
+    desc = prefill_desc(q, v, g, N, sd, scale, initial_state.shape[0] if pool else 0)
+    o = torch.empty(T, hv, dv, dtype=q.dtype, device=dev)
+    if pool:
+        if initial_state is None:
+            raise ValueError("pool mode needs the pool as initial_state")
+        final = initial_state
+        fptr = None
+    else:
+        final = torch.empty(N, hv, dv, dk, dtype=sd, device=dev) if output_final_state else None
+        fptr = _ptr(final)
+    stream = _stream(dev)
+    need = workspace_size(desc)
+    ws = _workspace(dev, stream, need)
+    _check(lib().kda_chunk_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(cu_seqlens), _ptr(initial_state), _ptr(state_indices), fptr,
+                                   _ptr(o), _ptr(ws), ws.numel(), stream))
+    return o, final
+
+
+def recurrent_decode(q, k, v, g, beta, state_pool, state_indices, scale=1.0):
+    """One-token decode for B requests, in place on the state pool.  Returns o."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, 3)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32, 2)
+    _need(state_pool, "state_pool", None, 4)
+    _need(state_indices, "state_indices", torch.int32, 1)
+    B, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    desc = DecodeDesc(B, hk, hv, dk, dv, _io_dtype(q), _DT[state_pool.dtype],
+                      GATE_SCALAR if g.dim() == 2 else GATE_CHANNEL, float(scale), state_pool.shape[0])
+    o = torch.empty(B, hv, dv, dtype=q.dtype, device=q.device)
+    _check(lib().kda_recurrent_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(state_pool), _ptr(state_indices), _ptr(o), _stream(q.device)))
+    return o

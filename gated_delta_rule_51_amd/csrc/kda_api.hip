@@ -1,0 +1,172 @@
+// C ABI of libkda: host-side validation, workspace sizing and launch sequencing.
+// Declarations and the contract live in include/kda.h.
+#include <hip/hip_runtime.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+bool dtype_ok(int t) { return t == KDA_F32 || t == KDA_BF16; }
+bool gate_ok(int t) { return t == KDA_GATE_CHANNEL || t == KDA_GATE_SCALAR; }
+bool aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t io_size(int t) { return t == KDA_BF16 ? 2 : 4; }
+
+// Byte ranges [p, p + n) overlap?
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+kda_status check_desc(const kda_prefill_desc *d) {
+    if (!d) return KDA_ERR_NULL;
+    if (d->num_seqs < 0 || d->total_tokens < 0 || d->hk <= 0 || d->hv <= 0 || d->dk <= 0 ||
+        d->dv <= 0 || d->hv % d->hk != 0)
+        return KDA_ERR_SHAPE;
+    if (!dim_ok(d->dk) || !dim_ok(d->dv) || !dtype_ok(d->io_dtype) || !dtype_ok(d->state_dtype) ||
+        !gate_ok(d->gate))
+        return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+kda_status check_decode_desc(const kda_decode_desc *d) {
+    if (!d) return KDA_ERR_NULL;
+    if (d->batch < 0 || d->hk <= 0 || d->hv <= 0 || d->dk <= 0 || d->dv <= 0 ||
+        d->hv % d->hk != 0 || d->num_slots <= 0)
+        return KDA_ERR_SHAPE;
+    if (!dim_ok(d->dk) || !dim_ok(d->dv) || !dtype_ok(d->io_dtype) || !dtype_ok(d->state_dtype) ||
+        !gate_ok(d->gate))
+        return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+kda_status hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer or descriptor is NULL";
+    case KDA_ERR_SHAPE: return "inconsistent or non-positive sizes";
+    case KDA_ERR_UNSUPPORTED: return "unsupported head dim, dtype, gate kind or grid size";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_ALIAS: return "an output aliases an input";
+    case KDA_ERR_HIP: return "HIP launch or runtime error";
+    case KDA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+int32_t kda_version(void) { return 100; }
+
+size_t kda_chunk_prefill_workspace_size(const kda_prefill_desc *d) {
+    if (check_desc(d) != KDA_OK) return 0;
+    return kda::prefill_workspace_bytes(d->num_seqs, d->total_tokens, d->hv, d->dk, d->dv);
+}
+
+kda_status kda_chunk_prefill(const kda_prefill_desc *d, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const int32_t *cu_seqlens,
+                             void *state, const int32_t *state_indices, void *final_state, void *o,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    kda_status st = check_desc(d);
+    if (st != KDA_OK) return st;
+    const bool pool = state_indices != nullptr;
+    const long T = d->total_tokens, N = d->num_seqs;
+    if (!cu_seqlens) return KDA_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    if (pool) {
+        if (!state) return KDA_ERR_NULL;
+        if (d->num_slots <= 0) return KDA_ERR_SHAPE;
+        if (final_state && final_state != state) return KDA_ERR_ALIAS;
+    }
+    const void *ptrs[] = {q, k, v, g, beta, cu_seqlens, state, state_indices, final_state, o, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned(p)) return KDA_ERR_ALIGN;
+    const size_t need = kda::prefill_workspace_bytes(d->num_seqs, d->total_tokens, d->hv, d->dk, d->dv);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+    // o must not alias any input; a dense final_state must not alias inputs
+    // other than the initial state.
+    const size_t isz = io_size(d->io_dtype), ssz = io_size(d->state_dtype);
+    const size_t qk_b = (size_t)T * d->hk * d->dk * isz, v_b = (size_t)T * d->hv * d->dv * isz;
+    const size_t g_b = (size_t)T * d->hv * (d->gate == KDA_GATE_SCALAR ? 1 : d->dk) * 4;
+    const size_t be_b = (size_t)T * d->hv * 4, cu_b = (size_t)(N + 1) * 4;
+    const size_t rows = pool ? (size_t)d->num_slots : (size_t)N;
+    const size_t s_b = rows * d->hv * d->dv * d->dk * ssz;
+    const size_t o_b = (size_t)T * d->hv * d->dv * isz;
+    struct R { const void *p; size_t n; } ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {g, g_b}, {beta, be_b},
+                                                   {cu_seqlens, cu_b}, {state, s_b},
+                                                   {state_indices, pool ? (size_t)N * 4 : 0},
+                                                   {workspace, need}};
+    for (const R &r : ins)
+        if (overlap(o, o_b, r.p, r.n)) return KDA_ERR_ALIAS;
+    if (!pool && final_state) {
+        const size_t f_b = (size_t)N * d->hv * d->dv * d->dk * ssz;
+        for (const R &r : ins)
+            if (r.p != state && overlap(final_state, f_b, r.p, r.n)) return KDA_ERR_ALIAS;
+        if (state && final_state != state && overlap(final_state, f_b, state, s_b)) return KDA_ERR_ALIAS;
+    }
+    if (N == 0) return KDA_OK;
+    if (T == 0 && !final_state) return KDA_OK;
+
+    kda::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
+    a.state_in = state;
+    a.state_out = pool ? state : final_state;
+    a.indices = state_indices;
+    a.o = o;
+    a.num_seqs = d->num_seqs; a.total_tokens = d->total_tokens;
+    a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
+    a.num_slots = pool ? d->num_slots : 0;
+    a.scale = d->scale;
+    a.io_bf16 = d->io_dtype == KDA_BF16;
+    a.state_bf16 = d->state_dtype == KDA_BF16;
+    a.scalar_gate = d->gate == KDA_GATE_SCALAR;
+    return hip_status(kda::launch_prefill(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_recurrent_decode(const kda_decode_desc *d, const void *q, const void *k, const void *v,
+                                const float *g, const float *beta, void *state_pool,
+                                const int32_t *state_indices, void *o, void *stream) {
+    kda_status st = check_decode_desc(d);
+    if (st != KDA_OK) return st;
+    if (d->batch == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !o) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, state_pool, state_indices, o};
+    for (const void *p : ptrs)
+        if (!aligned(p)) return KDA_ERR_ALIGN;
+    const size_t isz = io_size(d->io_dtype), B = d->batch;
+    const size_t o_b = B * d->hv * d->dv * isz;
+    struct R { const void *p; size_t n; } ins[] = {
+        {q, B * d->hk * d->dk * isz}, {k, B * d->hk * d->dk * isz}, {v, o_b},
+        {g, B * d->hv * (d->gate == KDA_GATE_SCALAR ? 1 : d->dk) * 4}, {beta, B * d->hv * 4},
+        {state_pool, (size_t)d->num_slots * d->hv * d->dv * d->dk * io_size(d->state_dtype)},
+        {state_indices, B * 4}};
+    for (const R &r : ins)
+        if (overlap(o, o_b, r.p, r.n)) return KDA_ERR_ALIAS;
+
+    // Grid (dv / tile, B, hv) must fit the device's per-axis limits.
+    int dev = 0, max_y = 0, max_z = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_z, hipDeviceAttributeMaxGridDimZ, dev) != hipSuccess)
+        return KDA_ERR_HIP;
+    if ((long)d->batch > max_y || (long)d->hv > max_z) return KDA_ERR_UNSUPPORTED;
+
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state_pool;
+    a.indices = state_indices; a.o = o;
+    a.batch = d->batch; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
+    a.num_slots = d->num_slots; a.scale = d->scale;
+    a.io_bf16 = d->io_dtype == KDA_BF16;
+    a.state_bf16 = d->state_dtype == KDA_BF16;
+    a.scalar_gate = d->gate == KDA_GATE_SCALAR;
+    return hip_status(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

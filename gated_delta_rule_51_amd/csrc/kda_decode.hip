@@ -1,0 +1,175 @@
+// One-token recurrent decode of the gated delta rule against a state pool.
+//
+// Per (value tile, request b, value head h) one workgroup streams the BV rows
+// of the stored state pool[slot(b), h] ([V, K], K contiguous), applies
+//     S' = Diag(exp g) S;  u = beta (v - S'^T k);  S = S' + k u^T;  o = scale S^T q
+// row by row (each stored row j is one value channel, so rows are independent
+// given k, q, g), and writes the rows back in place.  The grid keeps batch and
+// head on separate axes (sglang PR 37317 digest, 实现拆解 item 1: folding them
+// into one axis overflowed the 65535 limit at large decode batches).  A
+// negative slot index selects the last pool row (PR 30169 digest, 实现拆解
+// item 3).
+//
+// Memory-bound: the state row block is read once and written once with
+// 16-byte accesses that are contiguous across the workgroup.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int DK, int BV, typename IO, typename ST, bool SCALAR>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+    constexpr int VEC = (sizeof(ST) == 4) ? 4 : 8;  // state elements per 16 B
+    constexpr int LPR = DK / VEC;                    // lanes per stored row
+    constexpr int RPP = 256 / LPR;                   // rows per pass
+    constexpr int NP = (BV + RPP - 1) / RPP;         // passes
+    static_assert(DK % VEC == 0 && LPR <= 64, "tile");
+
+    const int tid = threadIdx.x;
+    const int cg = tid % LPR;
+    const int r0 = tid / LPR;
+    const int b = blockIdx.y;
+    const int h = blockIdx.z;
+    const int j0 = blockIdx.x * BV;
+    const int hk_idx = h / (a.hv / a.hk);
+
+    int slot = a.indices[b];
+    if (slot < 0) slot = a.num_slots - 1;
+    ST *st = reinterpret_cast<ST *>(a.state) +
+             (((long)slot * a.hv + h) * a.dv + j0) * (long)DK;
+
+    // Issue every state load first.
+    float s[NP][VEC];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = r0 + p * RPP;
+        if (row < BV) {
+            const ST *src = st + (long)row * DK + cg * VEC;
+            if constexpr (VEC == 4) {
+                f32x4 x = load4(src);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[p][i] = x[i];
+            } else {
+                u32x4 w = *reinterpret_cast<const u32x4 *>(src);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s[p][2 * i] = __uint_as_float(w[i] << 16);
+                    s[p][2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+                }
+            }
+        }
+    }
+
+    const int c0 = cg * VEC;
+    float dec[VEC], kk[VEC], qq[VEC];
+    const IO *kp = reinterpret_cast<const IO *>(a.k) + ((long)b * a.hk + hk_idx) * DK + c0;
+    const IO *qp = reinterpret_cast<const IO *>(a.q) + ((long)b * a.hk + hk_idx) * DK + c0;
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4) {
+        f32x4 x = load4(kp + i), y = load4(qp + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kk[i + e] = x[e];
+            qq[i + e] = y[e];
+        }
+    }
+    if constexpr (SCALAR) {
+        const float d = exp_f(a.g[(long)b * a.hv + h]);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) dec[i] = d;
+    } else {
+        const float *gp = a.g + ((long)b * a.hv + h) * DK + c0;
+#pragma unroll
+        for (int i = 0; i < VEC; i += 4) {
+            f32x4 x = *reinterpret_cast<const f32x4 *>(gp + i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dec[i + e] = exp_f(x[e]);
+        }
+    }
+    const float beta = a.beta[(long)b * a.hv + h];
+    const IO *vp = reinterpret_cast<const IO *>(a.v) + ((long)b * a.hv + h) * a.dv + j0;
+    IO *op = reinterpret_cast<IO *>(a.o) + ((long)b * a.hv + h) * a.dv + j0;
+
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = r0 + p * RPP;
+        if (row < BV) {
+            float pk = 0.f;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                s[p][i] *= dec[i];
+                pk += s[p][i] * kk[i];
+            }
+            pk = group_sum<LPR>(pk);
+            const float u = beta * (io_traits<IO>::load(vp, row) - pk);
+            float pq = 0.f;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                s[p][i] += kk[i] * u;
+                pq += s[p][i] * qq[i];
+            }
+            pq = group_sum<LPR>(pq);
+            if (cg == 0) io_traits<IO>::store(op, row, a.scale * pq);
+        }
+    }
+
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = r0 + p * RPP;
+        if (row < BV) {
+            ST *dst = st + (long)row * DK + cg * VEC;
+            if constexpr (VEC == 4) {
+                f32x4 x;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = s[p][i];
+                *reinterpret_cast<f32x4 *>(dst) = x;
+            } else {
+                u32x4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(s[p][2 * i], s[p][2 * i + 1]);
+                *reinterpret_cast<u32x4 *>(dst) = w;
+            }
+        }
+    }
+}
+
+template <int DK, int BV, typename IO, typename ST, bool SCALAR>
+static hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
+    dim3 grid(a.dv / BV, a.batch, a.hv);
+    decode_kernel<DK, BV, IO, ST, SCALAR><<<grid, 256, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int DK, int BV, typename IO, typename ST>
+static hipError_t launch_g(const DecodeArgs &a, hipStream_t s) {
+    return a.scalar_gate ? launch_t<DK, BV, IO, ST, true>(a, s) : launch_t<DK, BV, IO, ST, false>(a, s);
+}
+template <int DK, int BV, typename IO>
+static hipError_t launch_s(const DecodeArgs &a, hipStream_t s) {
+    return a.state_bf16 ? launch_g<DK, BV, IO, bf16>(a, s) : launch_g<DK, BV, IO, float>(a, s);
+}
+template <int DK, int BV>
+static hipError_t launch_i(const DecodeArgs &a, hipStream_t s) {
+    return a.io_bf16 ? launch_s<DK, BV, bf16>(a, s) : launch_s<DK, BV, float>(a, s);
+}
+template <int DK>
+static hipError_t launch_v(const DecodeArgs &a, int bv, hipStream_t s) {
+    switch (bv) {
+    case 32: return launch_i<DK, 32>(a, s);
+    case 64: return launch_i<DK, 64>(a, s);
+    default: return launch_i<DK, 128>(a, s);
+    }
+}
+
+int decode_tile(int dv) { return dv < 64 ? dv : 64; }
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+    const int bv = decode_tile(a.dv);
+    switch (a.dk) {
+    case 32: return launch_v<32>(a, bv, stream);
+    case 64: return launch_v<64>(a, bv, stream);
+    default: return launch_v<128>(a, bv, stream);
+    }
+}
+
+}  // namespace kda

@@ -1,0 +1,47 @@
+// Internal launch interface between the C ABI (kda_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    void *state;
+    const int32_t *indices;
+    void *o;
+    int batch, hk, hv, dk, dv, num_slots;
+    float scale;
+    bool io_bf16, state_bf16, scalar_gate;
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+int decode_tile(int dv);
+
+// Chunked prefill.  Chunk size and the chunk-slot bound are fixed here.
+constexpr int kChunk = 64;
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const int32_t *cu_seqlens;
+    const void *state_in;     // dense h0, pool, or NULL
+    void *state_out;          // dense ht, pool, or NULL
+    const int32_t *indices;   // pool slots or NULL
+    void *o;
+    int num_seqs, total_tokens, hk, hv, dk, dv, num_slots;
+    float scale;
+    bool io_bf16, state_bf16, scalar_gate;
+    // workspace carve-up (device pointers into the caller's buffer)
+    int chunk_slots;          // upper bound on the number of chunks
+    int32_t *chunk_map;       // [chunk_slots] (seq << 16 | local) or -1
+    void *ws_rest;            // chunk-level intermediates
+};
+
+size_t prefill_workspace_bytes(int num_seqs, int total_tokens, int hv, int dk, int dv);
+hipError_t launch_prefill(PrefillArgs &a, void *workspace, hipStream_t stream);
+
+}  // namespace kda

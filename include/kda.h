@@ -1,0 +1,162 @@
+/*
+ * libkda — gated delta rule (Kimi Delta Attention, KDA) on AMD Instinct MI355X
+ * (gfx950): chunked prefill over packed variable-length sequences and a
+ * one-token recurrent decode, both reading and writing recurrent states
+ * either densely or in place in a state pool.
+ *
+ * The operation (per sequence and value head; S is the K x V state):
+ *     S'  = Diag(exp g_t) S          decay, one factor per key channel
+ *     u   = beta_t (v_t - S'^T k_t)  delta-rule residual
+ *     S   = S' + k_t u^T             rank-1 write
+ *     o_t = scale * S^T q_t          read-out after the write
+ * GDN's scalar gate is the case of one g per (token, head) (gate = SCALAR).
+ *
+ * Sources (web digests of sglang pull requests):
+ *   - PR 27488 digest "KDA SM100 CuteDSL prefill": sections 功能与动机 and
+ *     实现拆解 (per-channel decay gate; chunk size 64; prologue cumsum, KKT
+ *     inverse + U/W, state and output kernels; workspace reuse keyed by
+ *     stream), and the extend wrapper in 关键源码片段 (q, k L2-normalised by
+ *     the caller; g and beta trimmed to the real token count).
+ *   - PR 30169 digest "fused pool-state I/O": sections 实现拆解 and 关键源码片段
+ *     (state pool [slots, Hv, V, K]; per-sequence slot indices read and
+ *     written in place by the state kernel; padding index -1 selects the last
+ *     slot; rows not indexed are untouched; pool mode bit-identical to dense).
+ *   - PR 37317 digest "grid split": section 实现拆解 item 1 (decode grid keeps
+ *     batch and head on separate axes, so B * Hv may exceed 65535).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *     in the layouts below, 16-byte aligned.  The library allocates nothing,
+ *     frees nothing and keeps no pointer after it returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns without synchronising the host.  No host<->device copies.
+ *   - Errors are found from host-visible values only (descriptor, null and
+ *     aligned pointers, workspace size, aliasing rules, grid limits) and are
+ *     reported as a status; nothing is launched when a check fails.  A launch
+ *     failure is reported as KDA_ERR_HIP.  Nothing prints, aborts or throws.
+ *   - Not checked (preconditions): device index values lie in [-1, slots-1]
+ *     and are unique apart from -1; g is finite and <= 0; cu_seqlens is
+ *     non-decreasing with cu[0] = 0 and cu[N] = total_tokens.
+ *   - GQA: value head h reads key head h / (hv / hk); hv % hk == 0.
+ *   - Supported sizes: dk, dv in {32, 64, 128}.  io dtype f32 or bf16; state
+ *     dtype f32 or bf16.  Accumulation is fp32.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    KDA_ERR_SHAPE = 2,       /* inconsistent or non-positive sizes              */
+    KDA_ERR_UNSUPPORTED = 3, /* dk/dv/dtype/gate outside the compiled set, or a
+                                grid beyond the device's limits                  */
+    KDA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required          */
+    KDA_ERR_ALIAS = 5,       /* an output aliases an input it must not alias     */
+    KDA_ERR_HIP = 6,         /* a HIP launch or runtime call failed              */
+    KDA_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned          */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+    KDA_GATE_CHANNEL = 0, /* KDA: g [T, hv, dk], one log-decay per key channel */
+    KDA_GATE_SCALAR = 1   /* GDN: g [T, hv], one log-decay per head            */
+} kda_gate;
+
+/* Host-side description of one prefill call. */
+typedef struct {
+    int32_t num_seqs;     /* N >= 0                                           */
+    int32_t total_tokens; /* T >= 0, equals cu_seqlens[N] on the device        */
+    int32_t hk, hv;       /* key heads, value heads (hv % hk == 0)             */
+    int32_t dk, dv;       /* key / value head dims                             */
+    int32_t io_dtype;     /* kda_dtype of q, k, v and o                        */
+    int32_t state_dtype;  /* kda_dtype of initial / final states and pools     */
+    int32_t gate;         /* kda_gate                                          */
+    float scale;          /* read-out scale applied to o                       */
+    int32_t num_slots;    /* pool rows (pool mode only; ignored in dense mode) */
+} kda_prefill_desc;
+
+/*
+ * Bytes of device workspace kda_chunk_prefill needs for `desc` (0 if the
+ * descriptor is invalid).  One workspace may be reused by any number of calls
+ * that are ordered on one stream; two streams must not share one at a time.
+ * The size grows linearly with T and N (chunk-level intermediates of the
+ * method, PR 27488 digest 实现拆解: U/W and pre-scaled operands per token).
+ */
+size_t kda_chunk_prefill_workspace_size(const kda_prefill_desc *desc);
+
+/*
+ * Chunked prefill over packed sequences (chunk size 64).
+ *   q, k        [T, hk, dk]  io dtype (callers pass L2-normalised q, k)
+ *   v           [T, hv, dv]  io dtype
+ *   g           [T, hv, dk] (CHANNEL) or [T, hv] (SCALAR), fp32, <= 0
+ *   beta        [T, hv] fp32
+ *   cu_seqlens  [N + 1] int32 (device)
+ *   state       dense mode (state_indices == NULL): initial states
+ *               [N, hv, dv, dk] state dtype, or NULL for zeros;
+ *               pool mode: the pool [num_slots, hv, dv, dk], required.
+ *   state_indices  NULL (dense mode) or [N] int32 slot per sequence; an index
+ *               < 0 selects slot num_slots - 1 (sentinel).
+ *   final_state dense mode: [N, hv, dv, dk] written with the final states, or
+ *               NULL (not written); may equal `state` (in place).
+ *               pool mode: must be NULL or equal to `state`; the final state of
+ *               sequence n is written to the same pool row it was read from.
+ *               Rows not indexed are neither read nor written.  With several
+ *               negative indices the sentinel row's content is unspecified.
+ *   o           [T, hv, dv] io dtype; must not alias any input.
+ *   workspace   device buffer of at least kda_chunk_prefill_workspace_size().
+ * A sequence of length 0 writes no o rows and leaves its state unchanged
+ * (copied to final_state in dense mode).  Pool mode and dense mode run the
+ * same kernels with the same tiling and produce bit-identical o and states.
+ */
+kda_status kda_chunk_prefill(const kda_prefill_desc *desc,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const int32_t *cu_seqlens,
+                             void *state, const int32_t *state_indices,
+                             void *final_state, void *o,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Host-side description of one decode call. */
+typedef struct {
+    int32_t batch;        /* B >= 0 requests, one token each                  */
+    int32_t hk, hv, dk, dv;
+    int32_t io_dtype, state_dtype, gate;
+    float scale;
+    int32_t num_slots;    /* pool rows                                         */
+} kda_decode_desc;
+
+/*
+ * One-token recurrent decode for B requests against a state pool, in place.
+ *   q, k  [B, hk, dk] io dtype;  v [B, hv, dv] io dtype
+ *   g     [B, hv, dk] (CHANNEL) or [B, hv] (SCALAR) fp32;  beta [B, hv] fp32
+ *   state_pool     [num_slots, hv, dv, dk] state dtype, read and written in place
+ *   state_indices  [B] int32; an index < 0 selects slot num_slots - 1
+ *   o     [B, hv, dv] io dtype
+ * The launch grid is (dv / tile, B, hv): batch and head on separate axes.
+ */
+kda_status kda_recurrent_decode(const kda_decode_desc *desc,
+                                const void *q, const void *k, const void *v,
+                                const float *g, const float *beta,
+                                void *state_pool, const int32_t *state_indices,
+                                void *o, void *stream);
+
+/* Static description of a status code. */
+const char *kda_status_string(kda_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/kda.h declares, and rejects bad arguments before any HIP call.
+
+Fake (host, never dereferenced) 16-byte-aligned pointer values are used; every
+call here returns from host-side validation, so no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_51_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL, SHAPE, UNSUP, WS, ALIAS, HIP, ALIGN = range(8)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.library_path()):
+        from gated_delta_rule_51_amd import build
+        build.build()
+    return kda.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_recurrent_decode",
+            "kda_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.kda_status_string(s).decode()
+    assert L.kda_version() >= 100
+
+
+def desc(**kw):
+    d = dict(num_seqs=2, total_tokens=100, hk=2, hv=4, dk=128, dv=128, io_dtype=1, state_dtype=0,
+             gate=0, scale=1.0, num_slots=0)
+    d.update(kw)
+    return kda.PrefillDesc(**d)
+
+
+# distinct, far-apart, 16-byte aligned fake addresses
+BASE = 1 << 40
+def fake(i, off=0):
+    return BASE + i * (1 << 32) + off
+
+
+def prefill(L, d, **over):
+    args = dict(q=fake(1), k=fake(2), v=fake(3), g=fake(4), beta=fake(5), cu=fake(6), state=None,
+                idx=None, final=fake(7), o=fake(8), ws=fake(9), wsb=1 << 40)
+    args.update(over)
+    return L.kda_chunk_prefill(ctypes.byref(d), args["q"], args["k"], args["v"], args["g"], args["beta"],
+                               args["cu"], args["state"], args["idx"], args["final"], args["o"],
+                               args["ws"], args["wsb"], None)
+
+
+def test_prefill_descriptor_errors(L):
+    assert L.kda_chunk_prefill(None, *([None] * 11), 0, None) == NULL
+    assert prefill(L, desc(hv=3)) == SHAPE            # hv % hk != 0
+    assert prefill(L, desc(hk=0)) == SHAPE
+    assert prefill(L, desc(num_seqs=-1)) == SHAPE
+    assert prefill(L, desc(dk=96)) == UNSUP
+    assert prefill(L, desc(dv=256)) == UNSUP
+    assert prefill(L, desc(io_dtype=7)) == UNSUP
+    assert prefill(L, desc(gate=5)) == UNSUP
+
+
+def test_prefill_pointer_errors(L):
+    d = desc()
+    assert prefill(L, d, q=None) == NULL
+    assert prefill(L, d, cu=None) == NULL
+    assert prefill(L, d, o=None) == NULL
+    assert prefill(L, d, q=fake(1, 4)) == ALIGN
+    assert prefill(L, d, ws=None) == WS
+    assert prefill(L, d, wsb=16) == WS
+    # pool mode: pool required, final_state must be NULL or the pool
+    dp = desc(num_slots=8)
+    assert prefill(L, dp, idx=fake(10), state=None) == NULL
+    assert prefill(L, dp, idx=fake(10), state=fake(11), final=fake(7)) == ALIAS
+    assert prefill(L, desc(num_slots=0), idx=fake(10), state=fake(11), final=None) == SHAPE
+
+
+def test_prefill_alias_errors(L):
+    d = desc()
+    assert prefill(L, d, o=fake(1)) == ALIAS                 # o is q
+    assert prefill(L, d, o=fake(3, 256)) == ALIAS            # o overlaps v
+    assert prefill(L, d, final=fake(2)) == ALIAS             # dense ht over k
+
+
+def test_workspace_size(L):
+    assert L.kda_chunk_prefill_workspace_size(None) == 0
+    assert L.kda_chunk_prefill_workspace_size(ctypes.byref(desc(dk=48))) == 0
+    a = L.kda_chunk_prefill_workspace_size(ctypes.byref(desc(total_tokens=1000)))
+    b = L.kda_chunk_prefill_workspace_size(ctypes.byref(desc(total_tokens=5000)))
+    assert b >= a
+
+
+def ddesc(**kw):
+    d = dict(batch=4, hk=2, hv=4, dk=128, dv=128, io_dtype=1, state_dtype=0, gate=0, scale=1.0,
+             num_slots=16)
+    d.update(kw)
+    return kda.DecodeDesc(**d)
+
+
+def decode(L, d, **over):
+    args = dict(q=fake(1), k=fake(2), v=fake(3), g=fake(4), beta=fake(5), pool=fake(6), idx=fake(7),
+                o=fake(8))
+    args.update(over)
+    return L.kda_recurrent_decode(ctypes.byref(d), args["q"], args["k"], args["v"], args["g"],
+                                  args["beta"], args["pool"], args["idx"], args["o"], None)
+
+
+def test_decode_errors(L):
+    assert L.kda_recurrent_decode(None, *([None] * 9)) == NULL
+    assert decode(L, ddesc(hv=3)) == SHAPE
+    assert decode(L, ddesc(num_slots=0)) == SHAPE
+    assert decode(L, ddesc(dk=16)) == UNSUP
+    assert decode(L, ddesc(state_dtype=3)) == UNSUP
+    assert decode(L, ddesc(), pool=None) == NULL
+    assert decode(L, ddesc(), idx=None) == NULL
+    assert decode(L, ddesc(), o=fake(8, 8)) == ALIGN
+    assert decode(L, ddesc(), o=fake(6, 1024)) == ALIAS     # o inside the pool
+    assert decode(L, ddesc(batch=0), q=None) == OK          # nothing to do
