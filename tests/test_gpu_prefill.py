@@ -1,0 +1,188 @@
+"""GPU parity of the chunked prefill (kda_chunk_prefill) against the fp64
+oracle, through the C ABI, plus pool-vs-dense bit identity and edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import kda_workloads as W
+from gpu_util import (O_MAXABS, STATE_REL_BF16, STATE_REL_F32, dev, host, max_abs, rel_l2, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import gated_delta_rule_51_amd as kda
+    kda.lib()
+    return kda
+
+
+def run_dense(K, inp, h0=None, state_dtype=None):
+    h0 = inp.h0 if h0 is None else h0
+    o, ht = K.chunk_prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                            dev(inp.cu_seqlens), initial_state=dev(h0), scale=inp.scale,
+                            state_dtype=state_dtype)
+    torch.cuda.synchronize()
+    return o, ht
+
+
+def check(name, o, ht, o_ref, ht_ref, state_bf16=False):
+    og, hg = host(o), host(ht)
+    assert np.isfinite(og).all() and np.isfinite(hg).all()
+    e_o = max_abs(og, o_ref)
+    e_s = rel_l2(hg, ht_ref)
+    worst = max((rel_l2(hg[n, h], ht_ref[n, h]) for n in range(ht_ref.shape[0])
+                 for h in range(ht_ref.shape[1]) if np.linalg.norm(ht_ref[n, h]) > 0), default=0.0)
+    say("%s: o max-abs %.3e (|o| max %.2f)  state rel-L2 %.3e (worst unit %.3e)"
+        % (name, e_o, float(np.abs(o_ref).max()) if o_ref.size else 0.0, e_s, worst))
+    assert e_o <= O_MAXABS, name
+    assert e_s <= (STATE_REL_BF16 if state_bf16 else STATE_REL_F32), name
+
+
+def test_config1_single_sequence_fp32(K, oracle):
+    inp = W.config1()
+    o, ht = run_dense(K, inp)
+    o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
+    check("config1", o, ht, o_ref, ht_ref)
+    say("config1 o rel-L2 %.3e" % rel_l2(host(o), o_ref))
+
+
+def test_config2_varlen_gqa(K, oracle):
+    inp = W.config2()
+    o, ht = run_dense(K, inp)
+    o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=inp.h0)
+    check("config2", o, ht, o_ref, ht_ref)
+
+
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+def test_config3_pool_matches_dense_bitwise(K, oracle, state_dtype):
+    """Pool mode reproduces dense mode bit for bit: same o, the final states
+    land in the indexed rows (the -1 index in the sentinel row), and every
+    other row is untouched."""
+    inp = W.config3(state_dtype=state_dtype)
+    S = inp.pool.shape[0]
+    slots = oracle.map_slot(inp.indices.numpy(), S)
+    pool_before = inp.pool.clone()
+    h0_dense = pool_before[torch.as_tensor(slots)]
+    o_d, ht_d = run_dense(K, inp, h0=h0_dense)
+    pool = dev(inp.pool)
+    o_p, ht_p = K.chunk_prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                                dev(inp.cu_seqlens), initial_state=pool, state_indices=dev(inp.indices))
+    torch.cuda.synchronize()
+    assert ht_p is pool
+    assert torch.equal(o_p, o_d)
+    sl = torch.as_tensor(slots).cuda()
+    assert torch.equal(pool[sl], ht_d)
+    untouched = torch.ones(S, dtype=torch.bool)
+    untouched[torch.as_tensor(slots)] = False
+    assert torch.equal(pool.cpu()[untouched], pool_before[untouched])
+    o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=h0_dense)
+    check("config3-%s" % state_dtype, o_p, pool[sl], o_ref, ht_ref, state_bf16=state_dtype == "bf16")
+
+
+def test_config4_realistic_gates_full(K, oracle):
+    """The bench workload: 16 sequences of 512..4096 tokens, Hk = Hv = 32,
+    K = V = 128, realistic gates (in-chunk cumulative log-decay up to ~1e4),
+    fp32 pool of 32 slots.  Every output and every written row is compared."""
+    say("generating prefill workload (16 seqs, 512..4096 tokens, 32 heads)")
+    inp = W.config4()
+    S = inp.pool.shape[0]
+    slots = oracle.map_slot(inp.indices.numpy(), S)
+    pool_before = inp.pool.clone()
+    pool = dev(inp.pool)
+    o, _ = K.chunk_prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                           dev(inp.cu_seqlens), initial_state=pool, state_indices=dev(inp.indices))
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens,
+                                   h0=pool_before[torch.as_tensor(slots)])
+    check("config4", o, pool[torch.as_tensor(slots).cuda()], o_ref, ht_ref)
+    untouched = np.setdiff1d(np.arange(S), slots)
+    assert torch.equal(pool[torch.as_tensor(untouched).cuda()].cpu(), pool_before[torch.as_tensor(untouched)])
+
+
+@pytest.mark.parametrize("gate", ["moderate", "realistic"])
+def test_scalar_gate_gdn(K, oracle, gate):
+    inp = W.make_prefill(61, [200, 64, 1, 77], 2, 4, 128, 128, gate=gate, scalar_gate=True, h0="random")
+    o, ht = run_dense(K, inp)
+    o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=inp.h0)
+    check("gdn-%s" % gate, o, ht, o_ref, ht_ref)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (32, 32), (128, 64), (64, 128), (32, 128)])
+def test_head_dims(K, oracle, dk, dv):
+    inp = W.make_prefill(62 + dk + dv, [130, 5, 64], 1, 2, dk, dv, h0="random", scale=dk ** -0.5)
+    o, ht = run_dense(K, inp)
+    o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=inp.h0,
+                                   scale=inp.scale)
+    check("dims-%d-%d" % (dk, dv), o, ht, o_ref, ht_ref)
+
+
+def test_ragged_and_empty_sequences(K, oracle):
+    """Lengths at and around chunk boundaries, and empty sequences (their final
+    state equals the initial state)."""
+    lens = [0, 1, 63, 64, 65, 0, 127, 128, 129, 2]
+    inp = W.make_prefill(63, lens, 2, 2, 128, 128, h0="random")
+    o, ht = run_dense(K, inp)
+    o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=inp.h0)
+    check("ragged", o, ht, o_ref, ht_ref)
+    assert torch.equal(ht[0].cpu(), inp.h0[0]) and torch.equal(ht[5].cpu(), inp.h0[5])
+
+
+def test_zero_initial_state_and_no_final(K, oracle):
+    inp = W.make_prefill(64, [90, 40], 1, 1, 128, 128)
+    o, _ = K.chunk_prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                           dev(inp.cu_seqlens), output_final_state=False)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
+    assert max_abs(host(o), o_ref) <= O_MAXABS
+
+
+def test_split_continuation(K, oracle):
+    """prefill(x[:a]) then prefill(x[a:]) from the carried state equals
+    prefill(x), for split points inside and at chunk boundaries."""
+    inp = W.make_prefill(65, [300], 2, 4, 128, 128, h0="random")
+    o_full, ht_full = run_dense(K, inp)
+    for a in (64, 100):
+        sa, sb = slice(0, a), slice(a, 300)
+        cu_a = torch.tensor([0, a], dtype=torch.int32)
+        cu_b = torch.tensor([0, 300 - a], dtype=torch.int32)
+        oa, ha = K.chunk_prefill(dev(inp.q[sa]).contiguous(), dev(inp.k[sa]).contiguous(),
+                                 dev(inp.v[sa]).contiguous(), dev(inp.g[sa]).contiguous(),
+                                 dev(inp.beta[sa]).contiguous(), dev(cu_a), initial_state=dev(inp.h0))
+        ob, hb = K.chunk_prefill(dev(inp.q[sb]).contiguous(), dev(inp.k[sb]).contiguous(),
+                                 dev(inp.v[sb]).contiguous(), dev(inp.g[sb]).contiguous(),
+                                 dev(inp.beta[sb]).contiguous(), dev(cu_b), initial_state=ha)
+        torch.cuda.synchronize()
+        assert max_abs(host(torch.cat([oa, ob])), host(o_full)) <= O_MAXABS
+        assert rel_l2(host(hb), host(ht_full)) <= STATE_REL_F32
+
+
+def test_prefill_then_decode(K, oracle):
+    """A decode step after a prefill continues the same recurrence."""
+    inp = W.make_prefill(66, [70, 129], 2, 4, 128, 128, h0="random")
+    T = inp.q.shape[0]
+    o, ht = run_dense(K, inp)
+    nxt = W.make_decode(67, 2, 2, 4, 128, 128, num_slots=3)
+    pool = ht.clone()
+    idx = torch.tensor([0, 1], dtype=torch.int32).cuda()
+    od = K.recurrent_decode(dev(nxt.q), dev(nxt.k), dev(nxt.v), dev(nxt.g), dev(nxt.beta), pool, idx)
+    torch.cuda.synchronize()
+    # oracle: append the decode token to each sequence
+    cu = inp.cu_seqlens.numpy()
+    parts = {n: [] for n in ("q", "k", "v", "g", "beta")}
+    for s in range(2):
+        for name in parts:
+            src = getattr(inp, name)[cu[s]:cu[s + 1]]
+            parts[name].append(torch.cat([src, getattr(nxt, name)[s:s + 1]]))
+    cat = {n: torch.cat(p) for n, p in parts.items()}
+    cu2 = torch.tensor([0, 71, 201], dtype=torch.int32)
+    o_ref, ht_ref = oracle.prefill(cat["q"], cat["k"], cat["v"], cat["g"], cat["beta"], cu2, h0=inp.h0)
+    assert max_abs(host(od), o_ref[[70, 200]]) <= O_MAXABS
+    assert rel_l2(host(pool), ht_ref) <= STATE_REL_F32
+
+
+def test_deterministic(K):
+    inp = W.make_prefill(68, [200, 33, 128], 2, 4, 128, 128, h0="random")
+    a = run_dense(K, inp)
+    b = run_dense(K, inp)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
