@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * chunked prefill (metadata, intra-chunk and state/output kernels) of the
+    Kimi-Linear-shaped workload: 16 sequences with lengths U{512..4096}
+    (seed 4: T = 38,632 tokens), Hk = Hv = 32, K = V = 128, bf16 q/k/v,
+    realistic per-channel gates, fp32 state pool of 32 slots updated in place;
+  * one-token recurrent decode of 4096 requests, Hk = Hv = 32, K = V = 128,
+    bf16 q/k/v, fp32 state pool of 4160 slots updated in place.
+Inputs are generated on the host (seeded), copied to HBM before timing, and
+stay resident.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2516.6    # MI355X dense fp16/bf16 MFMA, TFLOP/s
+
+METRIC = "KDA prefill tokens/s + MFMA util; decode states/s + HBM GB/s vs peak"
+
+
+def prefill_work(cu, hk, hv, dk, dv, chunk=64):
+    """Algorithmic flops and bytes of one prefill call.
+
+    flops per (token, value head): 6 K V (W S0, K~^T U, (Q G) S0) + C (3K + 2V)
+    (A, W, M and Ut, M U; triangles counted half).  Bytes: q, k (shared by the
+    Hv/Hk value heads of a key head), v, g (fp32 per channel), beta, o per
+    token-head, plus h0 read and ht written per (sequence, head) in fp32."""
+    T = int(cu[-1])
+    N = len(cu) - 1
+    flops = T * hv * (6 * dk * dv + chunk * (3 * dk + 2 * dv))
+    per_tok = 2 * dk * 2 * hk / hv + 2 * dv + 4 * dk + 4 + 2 * dv
+    nbytes = T * hv * per_tok + N * hv * 2 * 4 * dk * dv
+    return flops, nbytes
+
+
+def decode_work(B, hk, hv, dk, dv):
+    """Bytes per (request, head): fp32 state read + write, q, k, v, g, beta, o."""
+    per = 2 * 4 * dk * dv + (2 * dk * 2 * hk / hv + 2 * dv + 4 * dk + 4 + 2 * dv)
+    return B * hv * per
+
+
+def cpu_baseline(pre, dec):
+    """The fp64 oracle on the host cores, on a bounded sample of the same
+    workload: the full prefill batch (all 16 sequences, all heads) and 512 of
+    the 4096 decode requests."""
+    import numpy as np
+    from oracle import oracle as O
+    O.build(force=False)
+    threads = O.max_threads()
+    slots = O.map_slot(pre.indices.numpy(), pre.pool.shape[0])
+    h0 = pre.pool[slots]
+    t = time.perf_counter()
+    O.prefill(pre.q, pre.k, pre.v, pre.g, pre.beta, pre.cu_seqlens, h0=h0)
+    tp = time.perf_counter() - t
+    T = int(pre.cu_seqlens[-1])
+    nreq = 512
+    dslots = O.map_slot(dec.indices.numpy()[:nreq], dec.pool.shape[0])
+    t = time.perf_counter()
+    O.decode(dec.q[:nreq], dec.k[:nreq], dec.v[:nreq], dec.g[:nreq], dec.beta[:nreq], dec.pool[dslots])
+    td = time.perf_counter() - t
+    hv = dec.v.shape[1]
+    return {
+        "value": T / tp, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": "fp64 C oracle (OpenMP over sequence-head units): full prefill batch "
+                  "(%d tokens x 32 heads) in %.2f s; decode: %d of 4096 requests in %.3f s" % (T, tp, nreq, td),
+        "decode_states_per_s": nreq * hv / td,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--part", choices=["both", "prefill", "decode"], default="both",
+                    help="time one part only (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the KDA path has no cross-GPU step to time "
+              "(see the sharding note in DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kda_workloads as W
+    import gated_delta_rule_51_amd as kda
+
+    kda.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    pre = W.config4()
+    dec = W.config5()
+    P = {n: getattr(pre, n).to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens", "pool", "indices")}
+    D = {n: getattr(dec, n).to(dev) for n in ("q", "k", "v", "g", "beta", "pool", "indices")}
+    torch.cuda.synchronize()
+
+    do_pre = args.part in ("both", "prefill")
+    do_dec = args.part in ("both", "decode")
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        if do_pre:
+            kda.chunk_prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu_seqlens"],
+                              initial_state=P["pool"], state_indices=P["indices"])
+        if evs is not None:
+            evs[1].record()
+        if do_dec:
+            kda.recurrent_decode(D["q"], D["k"], D["v"], D["g"], D["beta"], D["pool"], D["indices"])
+        if evs is not None:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    finite = bool(torch.isfinite(P["pool"]).all().item()) and bool(torch.isfinite(D["pool"]).all().item())
+
+    cu = pre.cu_seqlens.tolist()
+    T = cu[-1]
+    hk, hv, dk, dv = 32, 32, 128, 128
+    pf, pb = prefill_work(cu, hk, hv, dk, dv)
+    B = dec.q.shape[0]
+    db = decode_work(B, hk, hv, dk, dv)
+
+    prefill = {"ms": pre_ms, "tokens_per_s": T / (pre_ms * 1e-3) if do_pre else None,
+               "tokens": T, "alg_tflops": pf / (pre_ms * 1e-9) / 1e3 if do_pre else None,
+               "alg_gbs": pb / (pre_ms * 1e-3) / 1e9 if do_pre else None}
+    if do_pre:
+        prefill["mfma_frac_alg"] = prefill["alg_tflops"] / MFMA_F16_PEAK_TFLOPS
+        prefill["hbm_frac_alg"] = prefill["alg_gbs"] / HBM_PEAK_GBS
+        prefill["roofline_frac"] = max(pf / (MFMA_F16_PEAK_TFLOPS * 1e12), pb / (HBM_PEAK_GBS * 1e9)) / (pre_ms * 1e-3)
+    decode = {"ms": dec_ms, "states_per_s": B * hv / (dec_ms * 1e-3) if do_dec else None,
+              "requests_per_s": B / (dec_ms * 1e-3) if do_dec else None,
+              "alg_gbs": db / (dec_ms * 1e-3) / 1e9 if do_dec else None}
+    if do_dec:
+        decode["hbm_frac_alg"] = decode["alg_gbs"] / HBM_PEAK_GBS
+
+    # dominant kernel: the decode kernel (one launch per step, timed by the
+    # events that bracket it on the stream it runs on)
+    if do_dec:
+        roof = {"kernel": "decode_kernel<128,64,bf16,float,false>", "bound": "hbm",
+                "achieved": decode["alg_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": decode["alg_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                "alg_bytes_per_launch": db}
+    else:
+        roof = {"kernel": "prefill (meta + intra + state)", "bound": "hbm",
+                "achieved": prefill["alg_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": prefill["alg_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                "alg_bytes_per_launch": pb}
+
+    out = {
+        "metric": METRIC,
+        "value": prefill["tokens_per_s"] if do_pre else decode["states_per_s"],
+        "unit": "tokens/s" if do_pre else "states/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "KDA chunked prefill: 16 seqs, lengths U{512..4096} (T=%d), Hk=Hv=32, "
+                               "K=V=128, bf16 q/k/v, realistic per-channel gates, fp32 pool 32 slots; "
+                               "+ recurrent decode: B=4096, Hk=Hv=32, K=V=128, fp32 pool 4160 slots" % T,
+                   "global_batch": len(cu) - 1, "seq_len": T, "parallelism": "single-gpu"},
+        "prefill": prefill, "decode": decode, "roofline": roof, "finite": finite,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pre, dec)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

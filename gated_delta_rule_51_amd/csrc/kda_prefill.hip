@@ -33,6 +33,8 @@
 // Operands are fp16 (bf16 q/k/v inputs convert exactly; fp16's 11-bit
 // significand keeps the final-state error near 4e-4 relative, where bf16
 // operands would exceed 1e-3); accumulation is fp32; the state stays fp32.
+#include <stdlib.h>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -156,26 +158,159 @@ __global__ __launch_bounds__(1024) void meta_kernel(const int32_t *cu, int n, Wo
     for (int s = total + tid; s < w.slots; s += 1024) w.chunk_map[s] = make_int2(-1, -1);
 }
 
+
+
+// 16x16 fp32 block helpers for one wave (lane layout of the 16x16x4 f32 MFMA).
+__device__ __forceinline__ f32x4 mm16(const float *X, int ldx, const float *Y, int ldy, int lane) {
+    const int m = lane & 15, kq = lane >> 4;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(X[m * ldx + 4 * kk + kq], Y[(4 * kk + kq) * ldy + m], acc);
+    return acc;
+}
+__device__ __forceinline__ void st16(float *Z, int ldz, const f32x4 &v, int lane) {
+    const int m = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) Z[(4 * kq + jj) * ldz + m] = v[jj];
+}
+// LDS writes of this wave are complete and visible to its other lanes.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+}
+
 // ---------------------------------------------------------------------------
-// intra: per (chunk slot, value head)
+// intra: per (chunk slot, value head), 512 threads
+//
+// Gate factors.  Thread f = (channel c, quarter q) owns tokens t = 16 q + tau,
+// tau = 0..15, of one key channel and keeps, per level l, the inclusive prefix
+// product P (within the aligned 2^l block) and the exclusive suffix product S
+// of a_t = exp(g_t).  At level l the pairs (r, i) whose highest differing bit
+// is l are split at the pivot p = last token of the first half of their
+// aligned 2^(l+1) block: exp(G_r - G_i) = P_l(r) * S_l(i), both <= 1.  Row
+// tokens (bit l set) give k P and q P, column tokens give k S; these operand
+// rows go to LDS in fp16 and two 16x16 MFMA tiles per t-half build A and M.
 // ---------------------------------------------------------------------------
+constexpr int NTI = 512;   // threads of the intra kernel
+
 template <int DK, int DV> struct IntraSmem {
-    _Float16 k16[C][DK + PADH];
-    _Float16 q16[C][DK + PADH];
     union {
-        _Float16 F[C][DK + PADH];  // gate factors of the current level
-        float scr[4][3][256];      // per-wave 16x16 fp32 scratch (inversion)
-    };
-    float A[C][C + 1];             // beta-scaled strictly-lower A; later T
-    float M[C][C + 1];             // M, then reused as T
-    _Float16 KGt[DK][C + PADH];    // (beta * K * exp(G))^T
-    _Float16 Vt[DV][C + PADH];     // (beta * V)^T
+        struct {
+            _Float16 Fk[C][DK + PADH];        // k * factor, every token
+            _Float16 Fq[C / 2][DK + PADH];    // q * factor, row tokens (bit l removed)
+        } f;
+        _Float16 stage[C][DK + PADH];         // Q exp(G) staging, later W staging
+        float scr[4][3][256];                 // inversion scratch (16x16 fp32 blocks)
+    } r1;
+    _Float16 KGt[DK][C + PADH];               // (beta K exp(G))^T
+    union {
+        float A[C][C + 1];                    // beta-scaled strictly-lower A
+        _Float16 Vt[DV][C];                   // (beta V)^T, 16 B chunks XOR-swizzled by row
+    } r3;
+    float T[C][C + 1];                        // M during the levels, then T = (I + A)^-1
     float beta[C];
-    float tot[2][DK];              // per-half gate totals
+    float qtot[4][DK];                        // per-quarter gate products
 };
 
+__device__ __forceinline__ int vt_col(int j, int t) { return t ^ ((j & 7) << 3); }
+
+template <int LVL> __device__ __forceinline__ bool row_bit(int qtr, int tau) {
+    if constexpr (LVL < 4) return (tau >> LVL) & 1;
+    else if constexpr (LVL == 4) return qtr & 1;
+    else return (qtr >> 1) & 1;
+}
+
+// Advance the chains from level LVL-1 to LVL and write this level's operand rows.
+template <int LVL, int DK, int DV>
+__device__ __forceinline__ void factor_level(float (&P)[16], float (&S)[16], const f16x2 (&kr)[8],
+                                             const f16x2 (&qr)[8], IntraSmem<DK, DV> &sm, int c, int qtr) {
+    if constexpr (LVL >= 1 && LVL <= 4) {
+        constexpr int hb = 1 << (LVL - 1);
+#pragma unroll
+        for (int tau = 0; tau < 16; ++tau)   // S first: it reads P of level LVL-1
+            if (((tau >> (LVL - 1)) & 1) == 0) S[tau] *= P[tau | (2 * hb - 1)];
+#pragma unroll
+        for (int tau = 15; tau >= 0; --tau)
+            if ((tau >> (LVL - 1)) & 1) P[tau] *= P[(tau & ~(2 * hb - 1)) + hb - 1];
+    } else if constexpr (LVL == 5) {
+        // blocks of 32 tokens span two quarters: use the partner quarter's total
+        if ((qtr & 1) == 0) {
+            const float tot = sm.qtot[qtr + 1][c];
+#pragma unroll
+            for (int tau = 0; tau < 16; ++tau) S[tau] *= tot;
+        } else {
+            const float tot = sm.qtot[qtr - 1][c];
+#pragma unroll
+            for (int tau = 0; tau < 16; ++tau) P[tau] *= tot;
+        }
+    }
+#pragma unroll
+    for (int tau = 0; tau < 16; ++tau) {
+        const int t = 16 * qtr + tau;
+        const float kv = (float)kr[tau >> 1][tau & 1];
+        if (row_bit<LVL>(qtr, tau)) {
+            sm.r1.f.Fk[t][c] = (_Float16)(kv * P[tau]);
+            const int ridx = ((t >> (LVL + 1)) << LVL) | (t & ((1 << LVL) - 1));
+            sm.r1.f.Fq[ridx][c] = (_Float16)((float)qr[tau >> 1][tau & 1] * P[tau]);
+        } else {
+            sm.r1.f.Fk[t][c] = (_Float16)(kv * S[tau]);
+        }
+    }
+    if constexpr (LVL == 4) sm.qtot[qtr][c] = P[15];   // quarter total (P over the whole quarter)
+}
+
+// MFMA tiles of level LVL: A (kind 0) and M (kind 1); valid pairs scattered to LDS.
+template <int LVL, int DK, int DV>
+__device__ __forceinline__ void mfma_level(IntraSmem<DK, DV> &sm, int wave, int lane) {
+    const int m = lane & 15, kq = lane >> 4;
+    int kind, rtok, ridx, ctok, rbase, cbase;
+    if constexpr (LVL < 5) {
+        if (wave >= 4) return;
+        const int th = wave & 1;
+        kind = wave >> 1;
+        rtok = 32 * th + insert_bit(m, LVL, 1);
+        ridx = 16 * th + m;
+        ctok = 32 * th + insert_bit(m, LVL, 0);
+        rbase = cbase = 32 * th;
+    } else {
+        const int tile = wave >> 1;
+        kind = wave & 1;
+        rbase = 32 + 16 * (tile >> 1);
+        cbase = 16 * (tile & 1);
+        rtok = rbase + m;
+        ridx = rtok - 32;
+        ctok = cbase + m;
+    }
+    const _Float16 *arow = kind == 0 ? &sm.r1.f.Fk[rtok][0] : &sm.r1.f.Fq[ridx][0];
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) {
+        const int c8 = kk * 32 + kq * 8;
+        acc = mfma_f16(lds8(arow + c8), lds8(&sm.r1.f.Fk[ctok][c8]), acc);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int orow = 4 * kq + jj;
+        int r, i;
+        bool valid;
+        if constexpr (LVL < 5) {
+            r = rbase + insert_bit(orow, LVL, 1);
+            i = cbase + insert_bit(m, LVL, 0);
+            valid = (orow >> LVL) == (m >> LVL);
+        } else {
+            r = rbase + orow;
+            i = cbase + m;
+            valid = true;
+        }
+        if (valid) {
+            if (kind == 0) sm.r3.A[r][i] = sm.beta[r] * acc[jj];
+            else sm.T[r][i] = acc[jj];
+        }
+    }
+}
+
 template <int DK, int DV, typename IO, bool SCALAR>
-__global__ __launch_bounds__(NT) void intra_kernel(PrefillArgs a, Work w) {
+__global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     IntraSmem<DK, DV> &sm = *reinterpret_cast<IntraSmem<DK, DV> *>(smem_raw);
 
@@ -187,335 +322,273 @@ __global__ __launch_bounds__(NT) void intra_kernel(PrefillArgs a, Work w) {
     const int L = min(C, a.cu_seqlens[n + 1] - t0);
     const int hk = h / (a.hv / a.hk);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t sh = (size_t)slot * a.hv + h;   // (slot, head) index
+    const size_t sh = (size_t)slot * a.hv + h;
 
     const IO *qg = reinterpret_cast<const IO *>(a.q);
     const IO *kg = reinterpret_cast<const IO *>(a.k);
     const IO *vg = reinterpret_cast<const IO *>(a.v);
 
-    // ---- phase 0: k, q -> fp16 LDS; beta; beta*V transposed; clear A, M ----
-    constexpr int KCH = DK / 8;   // 8-element chunks per row
-    for (int e = tid; e < C * KCH; e += NT) {
-        const int r = e / KCH, c8 = (e % KCH) * 8;
-        f16x8 kv = {}, qv = {};
-        if (r < L) {
-            const size_t off = ((size_t)(t0 + r) * a.hk + hk) * DK + c8;
-            kv = load8_f16<IO>(kg + off);
-            qv = load8_f16<IO>(qg + off);
-        }
-        *reinterpret_cast<f16x8 *>(&sm.k16[r][c8]) = kv;
-        *reinterpret_cast<f16x8 *>(&sm.q16[r][c8]) = qv;
-    }
-    if (tid < C) sm.beta[tid] = tid < L ? a.beta[(size_t)(t0 + tid) * a.hv + h] : 0.f;
-    for (int e = tid; e < C * (C + 1); e += NT) {
-        (&sm.A[0][0])[e] = 0.f;
-        (&sm.M[0][0])[e] = 0.f;
-    }
-    __syncthreads();
-    {
-        constexpr int TPJ = NT / DV;       // threads per value column
-        constexpr int TOK = C / TPJ;       // tokens per thread
-        const int j = tid % DV, part = tid / DV;
-        for (int i = 0; i < TOK; ++i) {
-            const int r = part * TOK + i;
-            float x = 0.f;
-            if (r < L) x = sm.beta[r] * io_traits<IO>::load(vg, ((size_t)(t0 + r) * a.hv + h) * DV + j);
-            sm.Vt[j][r] = (_Float16)x;
-        }
-    }
-
-    // ---- phase 1: gate factor chains, thread = (channel, half) ----
-    // P[tau]: inclusive prefix product of exp(g) within the aligned 2^l block,
-    // S[tau]: exclusive suffix product within the aligned 2^l block.
-    const bool fthread = tid < 2 * DK;
-    const int fc = tid % DK, fh = tid / DK;   // channel, half (valid if fthread)
-    float P[32], S[32];
+    // ---- phase 0: registers for the gate threads and the value threads ----
+    const bool fthread = tid < 4 * DK;
+    const int fc = tid % DK, fq = tid / DK;      // channel, quarter
+    float P[16], S[16];
+    f16x2 kr[8], qr[8];   // k, q rounded to fp16 (exact for bf16 inputs in range)
     if (fthread) {
 #pragma unroll
-        for (int tau = 0; tau < 32; ++tau) {
-            const int r = 32 * fh + tau;
-            float gv = 0.f;
+        for (int tau = 0; tau < 16; ++tau) {
+            const int r = 16 * fq + tau;
+            float gv = 0.f, kv = 0.f, qv = 0.f;
             if (r < L) {
-                if constexpr (SCALAR) gv = a.g[(size_t)(t0 + r) * a.hv + h];
-                else gv = a.g[((size_t)(t0 + r) * a.hv + h) * DK + fc];
+                const size_t t = t0 + r;
+                if constexpr (SCALAR) gv = a.g[t * a.hv + h];
+                else gv = a.g[(t * a.hv + h) * DK + fc];
+                kv = io_traits<IO>::load(kg, (t * a.hk + hk) * DK + fc);
+                qv = io_traits<IO>::load(qg, (t * a.hk + hk) * DK + fc);
             }
             P[tau] = exp_f(gv);
             S[tau] = 1.f;
+            kr[tau >> 1][tau & 1] = (_Float16)kv;
+            qr[tau >> 1][tau & 1] = (_Float16)qv;
         }
     }
+    if (tid < C) sm.beta[tid] = tid < L ? a.beta[(size_t)(t0 + tid) * a.hv + h] : 0.f;
+    // A: the diagonal blocks' diagonal and upper triangle are zero
+    for (int e = tid; e < 4 * 256; e += NTI) {
+        const int b = e >> 8, rr = (e >> 4) & 15, ii = e & 15;
+        if (ii >= rr) sm.r3.A[16 * b + rr][16 * b + ii] = 0.f;
+    }
+    __syncthreads();
 
+    // ---- levels 0..5: gate factors, then A and M tiles ----
 #pragma unroll
     for (int lvl = 0; lvl < 6; ++lvl) {
         if (fthread) {
-            if (lvl > 0) {
-                const int hb = 1 << (lvl - 1);     // sub-block size
-#pragma unroll
-                for (int tau = 0; tau < 32; ++tau) {
-                    // S update first (reads P of the previous level)
-                    if (((tau >> (lvl - 1)) & 1) == 0) {
-                        const int last2 = tau | ((hb << 1) - 1);   // last of 2nd sub-block
-                        S[tau] *= P[last2];
-                    }
-                }
-#pragma unroll
-                for (int tau = 31; tau >= 0; --tau) {
-                    if ((tau >> (lvl - 1)) & 1) {
-                        const int last1 = (tau & ~((hb << 1) - 1)) + hb - 1;   // last of 1st sub-block
-                        P[tau] *= P[last1];
-                    }
-                }
-            }
-            const int bitsrc = lvl;   // bit of the token index that selects row/col
-#pragma unroll
-            for (int tau = 0; tau < 32; ++tau) {
-                const int r = 32 * fh + tau;
-                const bool row = (r >> bitsrc) & 1;
-                sm.F[r][fc] = (_Float16)(row ? P[tau] : S[tau]);
+            switch (lvl) {
+            case 0: factor_level<0>(P, S, kr, qr, sm, fc, fq); break;
+            case 1: factor_level<1>(P, S, kr, qr, sm, fc, fq); break;
+            case 2: factor_level<2>(P, S, kr, qr, sm, fc, fq); break;
+            case 3: factor_level<3>(P, S, kr, qr, sm, fc, fq); break;
+            case 4: factor_level<4>(P, S, kr, qr, sm, fc, fq); break;
+            default: factor_level<5>(P, S, kr, qr, sm, fc, fq); break;
             }
         }
         __syncthreads();
-
-        // ---- MFMA tiles of this level: A (kind 0) and M (kind 1) ----
-        const int njobs = lvl < 5 ? 4 : 8;
-        for (int job = wave; job < njobs; job += 4) {
-            int kind, rows_base, cols_base, t_half;
-            if (lvl < 5) {
-                t_half = job & 1;
-                kind = job >> 1;
-                rows_base = cols_base = 0;
-            } else {
-                t_half = 0;
-                kind = job & 1;
-                const int tile = job >> 1;   // 0..3 -> (row tile, col tile)
-                rows_base = 32 + 16 * (tile >> 1);
-                cols_base = 16 * (tile & 1);
-            }
-            const int m = lane & 15, kq = lane >> 4;
-            int rtok, ctok;
-            if (lvl < 5) {
-                rtok = 32 * t_half + insert_bit(m, lvl, 1);
-                ctok = 32 * t_half + insert_bit(m, lvl, 0);
-            } else {
-                rtok = rows_base + m;
-                ctok = cols_base + m;
-            }
-            const _Float16 *src = kind == 0 ? &sm.k16[0][0] : &sm.q16[0][0];
-            f32x4 acc = zero4();
+        switch (lvl) {
+        case 0: mfma_level<0>(sm, wave, lane); break;
+        case 1: mfma_level<1>(sm, wave, lane); break;
+        case 2: mfma_level<2>(sm, wave, lane); break;
+        case 3: mfma_level<3>(sm, wave, lane); break;
+        case 4: mfma_level<4>(sm, wave, lane); break;
+        default: mfma_level<5>(sm, wave, lane); break;
+        }
+        if (lvl == 0 && wave >= 4) {
+            // diagonal of M: q_r . k_r (gate factor 1), four lanes per token
+            const int r = 16 * (wave - 4) + (lane >> 2), part = lane & 3;
+            float d = 0.f;
+            if (r < L) {
+                const size_t base = ((size_t)(t0 + r) * a.hk + hk) * DK + part * (DK / 4);
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const int c8 = kk * 32 + kq * 8;
-                f16x8 xr = lds8(src + rtok * (DK + PADH) + c8) * lds8(&sm.F[rtok][c8]);
-                f16x8 yc = lds8(&sm.k16[ctok][c8]) * lds8(&sm.F[ctok][c8]);
-                acc = mfma_f16(xr, yc, acc);
-            }
-            // scatter the valid pairs (same aligned 2^(lvl+1) block)
+                for (int e = 0; e < DK / 4; e += 4) {
+                    const f32x4 x = load4(qg + base + e), y = load4(kg + base + e);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int orow = 4 * kq + jj, ocol = m;
-                int r, i;
-                if (lvl < 5) {
-                    r = 32 * t_half + insert_bit(orow, lvl, 1);
-                    i = 32 * t_half + insert_bit(ocol, lvl, 0);
-                } else {
-                    r = rows_base + orow;
-                    i = cols_base + ocol;
-                }
-                if ((r >> (lvl + 1)) == (i >> (lvl + 1))) {
-                    if (kind == 0) sm.A[r][i] = sm.beta[r] * acc[jj];
-                    else sm.M[r][i] = acc[jj];
+                    for (int u = 0; u < 4; ++u) d += (float)(_Float16)x[u] * (float)(_Float16)y[u];
                 }
             }
+            d += __shfl_xor(d, 1, 64);
+            d += __shfl_xor(d, 2, 64);
+            if (part == 0) sm.T[r][r] = d;
         }
         __syncthreads();
     }
 
-    // ---- diagonal of M: q_r . k_r (factor 1), from 16x16 diagonal tiles ----
-    {
-        const int m = lane & 15, kq = lane >> 4;
-        const int base = 16 * wave;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            const int c8 = kk * 32 + kq * 8;
-            acc = mfma_f16(lds8(&sm.q16[base + m][c8]), lds8(&sm.k16[base + m][c8]), acc);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            if (4 * kq + jj == m) sm.M[base + m][base + m] = acc[jj];
-    }
-
-    // ---- chunk-level factors: exp(G_r) and exp(G_last - G_r) ----
-    if (fthread) {
-        // P[tau] now = prefix product within the half, S[tau] = suffix within the half
-        sm.tot[fh][fc] = P[31];
-    }
-    __syncthreads();
+    // ---- chunk-level factors: exp(G_t), exp(G_last - G_t) ----
     const size_t qg_off = sh * C * DK, kl_off = sh * DK * C;
     if (fthread) {
-        const float t0v = sm.tot[0][fc], t1v = sm.tot[1][fc];
-        if (fh == 0) w.GL[sh * DK + fc] = t0v * t1v;
+        const float h0t = sm.qtot[0][fc] * sm.qtot[1][fc], h1t = sm.qtot[2][fc] * sm.qtot[3][fc];
+        if (fq == 0) w.GL[sh * DK + fc] = h0t * h1t;
 #pragma unroll
-        for (int tau = 0; tau < 32; ++tau) {
-            const int r = 32 * fh + tau;
-            const float gam = fh ? P[tau] * t0v : P[tau];          // exp(G_r)
-            const float rest = fh ? S[tau] : S[tau] * t1v;         // exp(G_last - G_r)
-            const float kv = (float)sm.k16[r][fc];
-            const float qv = (float)sm.q16[r][fc];
-            sm.KGt[fc][r] = (_Float16)(sm.beta[r] * kv * gam);
-            w.QG[qg_off + (size_t)r * DK + fc] = (_Float16)(qv * gam);
-            w.KLt[kl_off + (size_t)fc * C + r] = (_Float16)(kv * rest);
-        }
-    }
-    __syncthreads();
-
-    // ---- store M (fp16) ----
-    for (int e = tid; e < C * C; e += NT) {
-        const int r = e / C, i = e % C;
-        w.M[sh * C * C + e] = (_Float16)sm.M[r][i];
-    }
-    __syncthreads();
-    // the T blocks above the block diagonal are zero
-    for (int e = tid; e < C * C; e += NT) {
-        const int r = e / C, i = e % C;
-        if ((i >> 4) > (r >> 4)) sm.M[r][i] = 0.f;
-    }
-
-    // ---- T = (I + A)^-1 into sm.M (blocked, fp32 MFMA) ----
-    // scratch for 16x16 fp32 blocks: reuse F (>= 4 waves x 3 x 1 KB)
-    float *scr = &sm.scr[wave][0][0];
-    auto mm16 = [&](const float *X, int ldx, const float *Y, int ldy) {
-        // 16x16 = X[16x16] * Y[16x16], fp32
-        const int m = lane & 15, kq = lane >> 4;
-        f32x4 acc = zero4();
+        for (int g8 = 0; g8 < 2; ++g8) {
+            f16x8 kgv, klv;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            acc = mfma_f32(X[m * ldx + 4 * kk + kq], Y[(4 * kk + kq) * ldy + m], acc);
-        return acc;
-    };
-    auto st16 = [&](float *Z, int ldz, const f32x4 &v) {
-        const int m = lane & 15, kq = lane >> 4;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) Z[(4 * kq + jj) * ldz + m] = v[jj];
-    };
-    auto ld16 = [&](const float *Z, int ldz) {
-        const int m = lane & 15, kq = lane >> 4;
-        f32x4 v;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v[jj] = Z[(4 * kq + jj) * ldz + m];
-        return v;
-    };
-    constexpr int LD = C + 1;
-    {
-        // diagonal block b = wave: (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8)
-        const int b = wave;
-        const float *Ab = &sm.A[16 * b][16 * b];
-        float *A2 = scr, *A4 = scr + 256, *X = scr + 512;
-        f32x4 v = mm16(Ab, LD, Ab, LD);
-        st16(A2, 16, v);
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
-        v = mm16(A2, 16, A2, 16);
-        st16(A4, 16, v);
-        // X = I - A + A^2 - A^3
-        f32x4 a3 = mm16(Ab, LD, A2, 16);
-        {
-            const int m = lane & 15, kq = lane >> 4;
-            f32x4 xv;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 4 * kq + jj;
-                xv[jj] = (r == m ? 1.f : 0.f) - Ab[r * LD + m] + A2[r * 16 + m] - a3[jj];
+            for (int e = 0; e < 8; ++e) {
+                const int tau = 8 * g8 + e, t = 16 * fq + tau;
+                const float gam = fq >= 2 ? P[tau] * h0t : P[tau];        // exp(G_t)
+                const float rest = fq < 2 ? S[tau] * h1t : S[tau];        // exp(G_last - G_t)
+                const float kv = (float)kr[tau >> 1][tau & 1], qv = (float)qr[tau >> 1][tau & 1];
+                kgv[e] = (_Float16)(sm.beta[t] * kv * gam);
+                klv[e] = (_Float16)(kv * rest);
+                sm.r1.stage[t][fc] = (_Float16)(qv * gam);
             }
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            st16(X, 16, xv);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            // X = X + X A^4
-            f32x4 t = mm16(X, 16, A4, 16);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) xv[jj] += t[jj];
-            // A^8 into A2
-            f32x4 a8 = mm16(A4, 16, A4, 16);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            st16(A2, 16, a8);
-            st16(X, 16, xv);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            t = mm16(X, 16, A2, 16);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) xv[jj] += t[jj];
-            st16(&sm.M[16 * b][16 * b], LD, xv);
+            *reinterpret_cast<f16x8 *>(&sm.KGt[fc][16 * fq + 8 * g8]) = kgv;
+            // (K exp(G_last - G))^T in A-operand tile layout: rows c, k index t
+            const int ln = (fc & 15) + 16 * (2 * (fq & 1) + g8);
+            *reinterpret_cast<f16x8 *>(w.KLt + kl_off + ((size_t)((fc >> 4) * 2 + (fq >> 1)) * 64 + ln) * 8) = klv;
         }
     }
     __syncthreads();
-    // off-diagonal blocks, by distance d = 1..3:  T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
+
+    // ---- A-operand tile stores: Q exp(G) and M (lower triangle incl. diagonal) ----
+    for (int e = tid; e < (C / 16) * (DK / 32) * 64; e += NTI) {
+        const int tile = e >> 6, l = e & 63;
+        const int rt = tile / (DK / 32), kk = tile % (DK / 32);
+        *reinterpret_cast<f16x8 *>(w.QG + qg_off + (size_t)e * 8) =
+            lds8(&sm.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]);
+    }
+    for (int e = tid; e < (C / 16) * (C / 32) * 64; e += NTI) {
+        const int tile = e >> 6, l = e & 63;
+        const int r = 16 * (tile >> 1) + (l & 15), i0 = 32 * (tile & 1) + 8 * (l >> 4);
+        f16x8 v;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (_Float16)(i0 + u <= r ? sm.T[r][i0 + u] : 0.f);
+        *reinterpret_cast<f16x8 *>(w.M + sh * C * C + (size_t)e * 8) = v;
+    }
+    __syncthreads();
+    // the blocks of T above the block diagonal are zero
+    for (int e = tid; e < C * C; e += NTI) {
+        const int r = e / C, i = e % C;
+        if ((i >> 4) > (r >> 4)) sm.T[r][i] = 0.f;
+    }
+
+    // ---- T = (I + A)^-1 (blocked, fp32 MFMA, waves 0..3); waves 4..7 load V ----
+    constexpr int TPJ = (NTI / 2) / DV;   // value threads per value column (waves 4..7)
+    constexpr int TOKV = C / TPJ;         // tokens per value thread
+    const int vt_id = tid - NTI / 2;
+    const int vj = vt_id % DV, vpart = vt_id / DV;
+    _Float16 vr[TOKV];
+    if (wave >= 4) {
+#pragma unroll
+        for (int i = 0; i < TOKV; ++i) {
+            const int r = vpart * TOKV + i;
+            vr[i] = (_Float16)(r < L ? io_traits<IO>::load(vg, ((size_t)(t0 + r) * a.hv + h) * DV + vj) : 0.f);
+        }
+    }
+    constexpr int LD = C + 1;
+    if (wave < 4) {
+        float *scr = &sm.r1.scr[wave][0][0];
+        const int b = wave;
+        const float *Ab = &sm.r3.A[16 * b][16 * b];
+        float *A2 = scr, *A4 = scr + 256, *X = scr + 512;
+        // (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) for strictly lower A
+        f32x4 v = mm16(Ab, LD, Ab, LD, lane);
+        st16(A2, 16, v, lane);
+        wave_sync();
+        v = mm16(A2, 16, A2, 16, lane);
+        st16(A4, 16, v, lane);
+        f32x4 a3 = mm16(Ab, LD, A2, 16, lane);
+        const int m = lane & 15, kq = lane >> 4;
+        f32x4 xv;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r = 4 * kq + jj;
+            xv[jj] = (r == m ? 1.f : 0.f) - Ab[r * LD + m] + A2[r * 16 + m] - a3[jj];
+        }
+        wave_sync();
+        st16(X, 16, xv, lane);
+        wave_sync();
+        f32x4 t = mm16(X, 16, A4, 16, lane);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) xv[jj] += t[jj];
+        f32x4 a8 = mm16(A4, 16, A4, 16, lane);
+        wave_sync();
+        st16(A2, 16, a8, lane);
+        st16(X, 16, xv, lane);
+        wave_sync();
+        t = mm16(X, 16, A2, 16, lane);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) xv[jj] += t[jj];
+        st16(&sm.T[16 * b][16 * b], LD, xv, lane);
+    }
+    __syncthreads();
+    // off-diagonal blocks by distance d: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
     for (int d = 1; d <= 3; ++d) {
-        const int nb = 4 - d;
-        if (wave < nb) {
+        if (wave < 4 - d) {
+            float *X = &sm.r1.scr[wave][0][0];
             const int b = wave, aa = b + d;
-            float *X = scr;
             f32x4 acc = zero4();
             for (int c = b; c < aa; ++c) {
-                f32x4 t = mm16(&sm.A[16 * aa][16 * c], LD, &sm.M[16 * c][16 * b], LD);
+                const f32x4 t = mm16(&sm.r3.A[16 * aa][16 * c], LD, &sm.T[16 * c][16 * b], LD, lane);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) acc[jj] += t[jj];
             }
-            st16(X, 16, acc);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            f32x4 tv = mm16(&sm.M[16 * aa][16 * aa], LD, X, 16);
+            st16(X, 16, acc, lane);
+            wave_sync();
+            f32x4 tv = mm16(&sm.T[16 * aa][16 * aa], LD, X, 16, lane);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) tv[jj] = -tv[jj];
-            st16(&sm.M[16 * aa][16 * b], LD, tv);
+            st16(&sm.T[16 * aa][16 * b], LD, tv, lane);
         }
         __syncthreads();
     }
-    // Inside each diagonal block the product form yields exact zeros above
-    // the diagonal (every term there is a sum of zero products).
 
-    // ---- W = T (beta K exp(G)),  Ut = T (beta V): wave = row tile ----
+    // ---- (beta V)^T into the (now free) A region ----
+    if (wave >= 4) {
+#pragma unroll
+        for (int i = 0; i < TOKV; ++i) {
+            const int r = vpart * TOKV + i;
+            sm.r3.Vt[vj][vt_col(vj, r)] = (_Float16)(sm.beta[r] * (float)vr[i]);
+        }
+    }
+    __syncthreads();
+
+    // ---- W = T (beta K exp(G)) -> LDS stage;  Ut = T (beta V) -> global acc tiles ----
     {
         const int m = lane & 15, kq = lane >> 4;
-        const int rt = wave;                    // rows 16 rt .. 16 rt + 15
+        const int rt = wave & 3, which = wave >> 2;
         f16x8 ta[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const float *tp = &sm.M[16 * rt + m][kk * 32 + kq * 8];
+            const float *tp = &sm.T[16 * rt + m][kk * 32 + kq * 8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) ta[kk][e] = (_Float16)tp[e];
         }
-        const int nk = (rt >> 1) + 1;           // k-steps that can be non-zero
-        _Float16 *Wg = w.W + sh * C * DK;
-        _Float16 *Ug = w.Ut + sh * C * DV;
+        const bool k1 = rt >= 2;   // T rows < 32 vanish for columns >= 32
+        if (which == 0) {
 #pragma unroll
-        for (int ct = 0; ct < DK / 16; ++ct) {
-            f32x4 acc = zero4();
-            for (int kk = 0; kk < nk; ++kk)
-                acc = mfma_f16(ta[kk], lds8(&sm.KGt[16 * ct + m][kk * 32 + kq * 8]), acc);
+            for (int ct = 0; ct < DK / 16; ++ct) {
+                f32x4 acc = mfma_f16(ta[0], lds8(&sm.KGt[16 * ct + m][kq * 8]), zero4());
+                if (k1) acc = mfma_f16(ta[1], lds8(&sm.KGt[16 * ct + m][32 + kq * 8]), acc);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                Wg[(size_t)(16 * rt + 4 * kq + jj) * DK + 16 * ct + m] = (_Float16)acc[jj];
+                for (int jj = 0; jj < 4; ++jj) sm.r1.stage[16 * rt + 4 * kq + jj][16 * ct + m] = (_Float16)acc[jj];
+            }
+        } else {
+            _Float16 *Ug = w.Ut + sh * C * DV;
+#pragma unroll
+            for (int ct = 0; ct < DV / 16; ++ct) {
+                const int j = 16 * ct + m;
+                f32x4 acc = mfma_f16(ta[0], lds8(&sm.r3.Vt[j][vt_col(j, kq * 8)]), zero4());
+                if (k1) acc = mfma_f16(ta[1], lds8(&sm.r3.Vt[j][vt_col(j, 32 + kq * 8)]), acc);
+                f16x4 h4;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) h4[jj] = (_Float16)acc[jj];
+                *reinterpret_cast<f16x4 *>(Ug + ((size_t)(rt * (DV / 16) + ct) * 64 + lane) * 4) = h4;
+            }
         }
-#pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct) {
-            f32x4 acc = zero4();
-            for (int kk = 0; kk < nk; ++kk)
-                acc = mfma_f16(ta[kk], lds8(&sm.Vt[16 * ct + m][kk * 32 + kq * 8]), acc);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                Ug[(size_t)(16 * rt + 4 * kq + jj) * DV + 16 * ct + m] = (_Float16)acc[jj];
+    }
+    __syncthreads();
+    {
+        _Float16 *Wg = w.W + sh * C * DK;
+        for (int e = tid; e < (C / 16) * (DK / 32) * 64; e += NTI) {
+            const int tile = e >> 6, l = e & 63;
+            const int rt = tile / (DK / 32), kk = tile % (DK / 32);
+            *reinterpret_cast<f16x8 *>(Wg + (size_t)e * 8) =
+                lds8(&sm.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // state: per (value tile, sequence, value head), sequential over chunks
+//
+// Operand layouts written by the intra kernel (fp16):
+//   A-operand tiles: tile (rt, kk) of an R x K matrix X holds, for lane l,
+//     X[16 rt + l % 16][32 kk + 8 (l / 16) + e], e = 0..7   (16 B per lane)
+//   accumulator tiles: tile (rt, ct) holds, for lane l,
+//     X[16 rt + 4 (l / 16) + jj][16 ct + l % 16], jj = 0..3  (8 B per lane)
+// so every operand load is one contiguous 16 B (or 8 B) access per lane.
 // ---------------------------------------------------------------------------
 template <int DK, int BV> struct StateSmem {
-    _Float16 Sh[BV][DK + PADH];   // S^T as fp16 (B operand of W S and Q S)
-    _Float16 Vn[BV][C + PADH];    // U^T as fp16 (B operand of M U and K^T U)
+    _Float16 Sh[BV][DK + PADH];   // S^T as fp16 (B operand of W S and QG S)
+    _Float16 Vn[BV][C + PADH];    // U^T as fp16 (B operand of M U and KLt U)
 };
 
 template <typename ST> __device__ __forceinline__ f32x4 load_state4(const ST *p);
@@ -531,9 +604,20 @@ __device__ __forceinline__ void store_state4(bf16 *p, const f32x4 &v) {
     *reinterpret_cast<u32x2 *>(p) = w;
 }
 
+__device__ __forceinline__ f16x8 gld8(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+__device__ __forceinline__ f16x4 gld4(const _Float16 *p) { return *reinterpret_cast<const f16x4 *>(p); }
+
 template <int DK, int DV, int BV, typename IO, typename ST>
 __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
     __shared__ __align__(16) StateSmem<DK, BV> sm;
+    constexpr int KK = DK / 32;          // k-steps over key channels
+    constexpr int CT = BV / 16;          // value column tiles of this workgroup
+    constexpr int R = DK / 16;           // key row tiles of the state
+    constexpr int WPR = R >= 4 ? 1 : 4 / R;   // waves sharing one state row tile
+    constexpr int RPW = R >= 4 ? R / 4 : 1;   // state row tiles per wave
+    constexpr int CTW = CT / WPR;             // state column tiles per wave
+    static_assert(CTW >= 1, "tile");
+
     const int vt = blockIdx.x, n = blockIdx.y, h = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, kq = lane >> 4;
@@ -541,13 +625,8 @@ __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
     const int tbeg = a.cu_seqlens[n], tend = a.cu_seqlens[n + 1];
     const int nchunks = (tend - tbeg + C - 1) / C;
     const int s0 = w.chunk_off[n];
-
-    // state tiles (rows = key channel c, cols = value j): wave owns tiles
-    // st = wave + 4 k, (rt, ct) = (st / (BV/16), st % (BV/16))
-    constexpr int CT = BV / 16;
-    constexpr int NST = (DK / 16) * CT;
-    constexpr int SPW = (NST + 3) / 4;   // state tiles per wave
-    f32x4 S[SPW];
+    const int rt0 = (wave / WPR) * RPW;       // first state row tile of this wave
+    const int ct0 = (wave % WPR) * CTW;       // first state column tile of this wave
 
     long row_in = -1, row_out = -1;
     if (a.indices) {
@@ -558,113 +637,111 @@ __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
         if (a.state_in) row_in = n;
         if (a.state_out) row_out = n;
     }
+    // S tiles: S[r][c] holds rows c = 16 (rt0 + r) + 4 kq + jj, cols j = 16 (ct0 + c) + m
+    f32x4 S[RPW][CTW];
     const ST *sin = row_in >= 0 ? reinterpret_cast<const ST *>(a.state_in) + ((size_t)row_in * a.hv + h) * DV * DK
                                 : nullptr;
 #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-        const int st = wave + 4 * q;
-        S[q] = zero4();
-        if (st < NST && sin) {
-            const int rt = st / CT, ct = st % CT;
-            // lane holds S[c = 16 rt + 4 kq + jj][j = 16 ct + m]; stored [V][K]
-            S[q] = load_state4<ST>(sin + (size_t)(j0 + 16 * ct + m) * DK + 16 * rt + 4 * kq);
-        }
-    }
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int c = 0; c < CTW; ++c)
+            S[r][c] = sin ? load_state4<ST>(sin + (size_t)(j0 + 16 * (ct0 + c) + m) * DK + 16 * (rt0 + r) + 4 * kq)
+                          : zero4();
 
     IO *og = reinterpret_cast<IO *>(a.o);
-
     for (int ch = 0; ch < nchunks; ++ch) {
         const size_t sh = (size_t)(s0 + ch) * a.hv + h;
         const int t0 = tbeg + ch * C;
         const int L = min(C, tend - t0);
+        // operands of this wave (row tile `wave` of the chunk's tokens)
+        const _Float16 *Wg = w.W + sh * C * DK + (size_t)wave * KK * 512 + lane * 8;
+        const _Float16 *Qg = w.QG + sh * C * DK + (size_t)wave * KK * 512 + lane * 8;
+        const _Float16 *Mg = w.M + sh * C * C + (size_t)wave * 2 * 512 + lane * 8;
+        const _Float16 *Ug = w.Ut + sh * C * DV + ((size_t)wave * (DV / 16) + vt * CT) * 256 + lane * 4;
+        const _Float16 *Kg = w.KLt + sh * DK * C + lane * 8;
+        const float *GLg = w.GL + sh * DK;
+        f16x8 Wa[KK], Qa[KK], Ma[2], Ka[RPW][2];
+        f16x4 Ua[CT];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            Wa[kk] = gld8(Wg + kk * 512);
+            Qa[kk] = gld8(Qg + kk * 512);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Ua[ct] = gld4(Ug + ct * 256);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) Ma[kk] = gld8(Mg + kk * 512);
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) Ka[r][kk] = gld8(Kg + ((size_t)(rt0 + r) * 2 + kk) * 512);
+        f32x4 gl[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) gl[r] = *reinterpret_cast<const f32x4 *>(GLg + 16 * (rt0 + r) + 4 * kq);
+
         // (a) S^T -> fp16 LDS
 #pragma unroll
-        for (int q = 0; q < SPW; ++q) {
-            const int st = wave + 4 * q;
-            if (st < NST) {
-                const int rt = st / CT, ct = st % CT;
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int c = 0; c < CTW; ++c) {
                 f16x4 hv4;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) hv4[jj] = (_Float16)S[q][jj];
-                *reinterpret_cast<f16x4 *>(&sm.Sh[16 * ct + m][16 * rt + 4 * kq]) = hv4;
+                for (int jj = 0; jj < 4; ++jj) hv4[jj] = (_Float16)S[r][c][jj];
+                *reinterpret_cast<f16x4 *>(&sm.Sh[16 * (ct0 + c) + m][16 * (rt0 + r) + 4 * kq]) = hv4;
             }
-        }
         __syncthreads();
-        // (b) U = Ut - W S  -> U^T fp16 in LDS; tiles (row tile rv = token, ct)
-        const _Float16 *Wg = w.W + sh * C * DK;
-        const _Float16 *Ug = w.Ut + sh * C * DV;
-        for (int ut = wave; ut < 4 * CT; ut += 4) {
-            const int rv = ut / CT, ct = ut % CT;
-            f32x4 acc = zero4();
+        // (b) U = Ut - W S and the inter-chunk part of O, row tile `wave`
+        f32x4 Oacc[CT];
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const int c8 = kk * 32 + kq * 8;
-                acc = mfma_f16(lds8(Wg + (size_t)(16 * rv + m) * DK + c8), lds8(&sm.Sh[16 * ct + m][c8]), acc);
+        for (int ct = 0; ct < CT; ++ct) {
+            f32x4 ws = zero4(), qs = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const f16x8 b = lds8(&sm.Sh[16 * ct + m][kk * 32 + kq * 8]);
+                ws = mfma_f16(Wa[kk], b, ws);
+                qs = mfma_f16(Qa[kk], b, qs);
             }
+            Oacc[ct] = qs;
             f16x4 uv;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 16 * rv + 4 * kq + jj;
-                const float u = (float)Ug[(size_t)r * DV + j0 + 16 * ct + m] - acc[jj];
-                uv[jj] = (_Float16)u;
-            }
-            *reinterpret_cast<f16x4 *>(&sm.Vn[16 * ct + m][16 * rv + 4 * kq]) = uv;
+            for (int jj = 0; jj < 4; ++jj) uv[jj] = (_Float16)((float)Ua[ct][jj] - ws[jj]);
+            *reinterpret_cast<f16x4 *>(&sm.Vn[16 * ct + m][16 * wave + 4 * kq]) = uv;
         }
         __syncthreads();
-        // (c) O = scale (QG S + M U)
-        const _Float16 *Qg = w.QG + sh * C * DK;
-        const _Float16 *Mg = w.M + sh * C * C;
-        for (int ot = wave; ot < 4 * CT; ot += 4) {
-            const int rv = ot / CT, ct = ot % CT;
-            f32x4 acc = zero4();
+        // (c) O += M U; write the valid rows
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const int c8 = kk * 32 + kq * 8;
-                acc = mfma_f16(lds8(Qg + (size_t)(16 * rv + m) * DK + c8), lds8(&sm.Sh[16 * ct + m][c8]), acc);
-            }
+        for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int i8 = kk * 32 + kq * 8;
-                acc = mfma_f16(lds8(Mg + (size_t)(16 * rv + m) * C + i8), lds8(&sm.Vn[16 * ct + m][i8]), acc);
-            }
+            for (int kk = 0; kk < 2; ++kk)
+                Oacc[ct] = mfma_f16(Ma[kk], lds8(&sm.Vn[16 * ct + m][kk * 32 + kq * 8]), Oacc[ct]);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int r = 16 * rv + 4 * kq + jj;
+                const int r = 16 * wave + 4 * kq + jj;
                 if (r < L)
                     io_traits<IO>::store(og, ((size_t)(t0 + r) * a.hv + h) * DV + j0 + 16 * ct + m,
-                                         a.scale * acc[jj]);
+                                         a.scale * Oacc[ct][jj]);
             }
         }
-        // (d) S = diag(exp G_last) S + (K exp(G_last - G))^T U
-        const _Float16 *Kl = w.KLt + sh * DK * C;
-        const float *GLg = w.GL + sh * DK;
+        // (d) S = diag(exp G_last) S + KLt U
 #pragma unroll
-        for (int q = 0; q < SPW; ++q) {
-            const int st = wave + 4 * q;
-            if (st < NST) {
-                const int rt = st / CT, ct = st % CT;
+        for (int r = 0; r < RPW; ++r)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) S[q][jj] *= GLg[16 * rt + 4 * kq + jj];
+            for (int c = 0; c < CTW; ++c) {
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int t8 = kk * 32 + kq * 8;
-                    S[q] = mfma_f16(lds8(Kl + (size_t)(16 * rt + m) * C + t8), lds8(&sm.Vn[16 * ct + m][t8]), S[q]);
-                }
+                for (int jj = 0; jj < 4; ++jj) S[r][c][jj] *= gl[r][jj];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    S[r][c] = mfma_f16(Ka[r][kk], lds8(&sm.Vn[16 * (ct0 + c) + m][kk * 32 + kq * 8]), S[r][c]);
             }
-        }
-        __syncthreads();
     }
 
     if (row_out >= 0) {
         ST *sout = reinterpret_cast<ST *>(a.state_out) + ((size_t)row_out * a.hv + h) * DV * DK;
 #pragma unroll
-        for (int q = 0; q < SPW; ++q) {
-            const int st = wave + 4 * q;
-            if (st < NST) {
-                const int rt = st / CT, ct = st % CT;
-                store_state4(sout + (size_t)(j0 + 16 * ct + m) * DK + 16 * rt + 4 * kq, S[q]);
-            }
-        }
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int c = 0; c < CTW; ++c)
+                store_state4(sout + (size_t)(j0 + 16 * (ct0 + c) + m) * DK + 16 * (rt0 + r) + 4 * kq, S[r][c]);
     }
 }
 
@@ -678,22 +755,31 @@ hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
     if (a.scalar_gate) {
         auto kern = intra_kernel<DK, DV, IO, true>;
         hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        kern<<<grid, NT, smem, s>>>(a, w);
+        kern<<<grid, NTI, smem, s>>>(a, w);
     } else {
         auto kern = intra_kernel<DK, DV, IO, false>;
         hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        kern<<<grid, NT, smem, s>>>(a, w);
+        kern<<<grid, NTI, smem, s>>>(a, w);
     }
+    return hipGetLastError();
+}
+
+template <int DK, int DV, int BV, typename IO>
+hipError_t launch_state_bv(PrefillArgs &a, Work &w, hipStream_t s) {
+    dim3 grid(DV / BV, a.num_seqs, a.hv);
+    if (a.state_bf16) state_kernel<DK, DV, BV, IO, bf16><<<grid, NT, 0, s>>>(a, w);
+    else state_kernel<DK, DV, BV, IO, float><<<grid, NT, 0, s>>>(a, w);
     return hipGetLastError();
 }
 
 template <int DK, int DV, typename IO>
 hipError_t launch_state(PrefillArgs &a, Work &w, hipStream_t s) {
-    constexpr int BV = DV < 32 ? DV : 32;
-    dim3 grid(DV / BV, a.num_seqs, a.hv);
-    if (a.state_bf16) state_kernel<DK, DV, BV, IO, bf16><<<grid, NT, 0, s>>>(a, w);
-    else state_kernel<DK, DV, BV, IO, float><<<grid, NT, 0, s>>>(a, w);
-    return hipGetLastError();
+    static const int bv_env = [] { const char *e = getenv("KDA_TUNE_STATE_BV"); return e ? atoi(e) : 0; }();
+    if constexpr (DV >= 64) {
+        if (bv_env == 32) return launch_state_bv<DK, DV, 32, IO>(a, w, s);
+        if (bv_env == 64) return launch_state_bv<DK, DV, 64, IO>(a, w, s);
+    }
+    return launch_state_bv<DK, DV, DV, IO>(a, w, s);
 }
 
 template <int DK, int DV, typename IO>
