@@ -28,6 +28,29 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2516.6    # MI355X dense fp16/bf16 MFMA, TFLOP/s
 
 METRIC = "KDA prefill tokens/s + MFMA util; decode states/s + HBM GB/s vs peak"
+DECODE_KERNEL = "kda::decode_kernel<128, 128, kda::bf16, float, false, true>"
+DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_51_amd", "csrc", "kda_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_config5_traffic.json")
+
+
+def _sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs recorded under profiles/ (scaled by a plain copy of known size), or
+    None when the decode source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != _sha(DECODE_SRC):
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def prefill_work(cu, hk, hv, dk, dv, chunk=64):
@@ -87,6 +110,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--part", choices=["both", "prefill", "decode"], default="both",
                     help="time one part only (for profiling runs)")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="run one plain device copy of this size first (a known-size "
+                         "reference for FETCH_SIZE / WRITE_SIZE counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the KDA path has no cross-GPU step to time "
@@ -106,6 +132,14 @@ def main():
     P = {n: getattr(pre, n).to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens", "pool", "indices")}
     D = {n: getattr(dec, n).to(dev) for n in ("q", "k", "v", "g", "beta", "pool", "indices")}
     torch.cuda.synchronize()
+
+    if args.copy_calibration_gib > 0:
+        nel = int(args.copy_calibration_gib * (1 << 30)) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     do_pre = args.part in ("both", "prefill")
     do_dec = args.part in ("both", "decode")
@@ -146,7 +180,7 @@ def main():
     db = decode_work(B, hk, hv, dk, dv)
 
     prefill = {"ms": pre_ms, "tokens_per_s": T / (pre_ms * 1e-3) if do_pre else None,
-               "tokens": T, "alg_tflops": pf / (pre_ms * 1e-9) / 1e3 if do_pre else None,
+               "tokens": T, "alg_tflops": pf / (pre_ms * 1e-3) / 1e12 if do_pre else None,
                "alg_gbs": pb / (pre_ms * 1e-3) / 1e9 if do_pre else None}
     if do_pre:
         prefill["mfma_frac_alg"] = prefill["alg_tflops"] / MFMA_F16_PEAK_TFLOPS
@@ -161,9 +195,9 @@ def main():
     # dominant kernel: the decode kernel (one launch per step, timed by the
     # events that bracket it on the stream it runs on)
     if do_dec:
-        roof = {"kernel": "decode_kernel<128,64,bf16,float,false>", "bound": "hbm",
+        roof = {"kernel": DECODE_KERNEL, "bound": "hbm",
                 "achieved": decode["alg_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": decode["alg_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                "frac": decode["alg_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                 "alg_bytes_per_launch": db}
     else:
         roof = {"kernel": "prefill (meta + intra + state)", "bound": "hbm",
