@@ -114,6 +114,17 @@ kda_status kda_chunk_prefill(const kda_prefill_desc *d, const void *q, const voi
     if (N == 0) return KDA_OK;
     if (T == 0 && !final_state) return KDA_OK;
 
+    // Grids: intra (chunk slots, hv); state 1-D over (value tiles x hv x N),
+    // padded to a multiple of 8.
+    int dev = 0, max_x = 0, max_y = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess)
+        return KDA_ERR_HIP;
+    const long slots = (T + 63L * N) / 64;
+    const long state_wgs = ((long)d->hv * N + 7) / 8 * 8 * 4;
+    if (slots > max_x || (long)d->hv > max_y || state_wgs > max_x) return KDA_ERR_UNSUPPORTED;
+
     kda::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
     a.state_in = state;

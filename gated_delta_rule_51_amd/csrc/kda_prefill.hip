@@ -43,6 +43,7 @@ namespace {
 constexpr int C = kChunk;   // 64
 constexpr int NT = 256;     // threads per workgroup
 constexpr int PADH = 8;     // fp16 row padding (16 B) against LDS bank conflicts
+constexpr int kOrderMax = 4096;   // sequences ranked by length in the meta kernel
 
 __device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -86,7 +87,7 @@ __device__ __forceinline__ f16x8 lds8(const _Float16 *p) { return *reinterpret_c
 // Workspace layout (per chunk slot s and value head h; all offsets 256-aligned)
 // ---------------------------------------------------------------------------
 struct Layout {
-    size_t chunk_map, chunk_off, W, Ut, M, QG, KLt, GL, total;
+    size_t chunk_map, chunk_off, seq_order, W, Ut, M, QG, KLt, GL, total;
     int slots;
 };
 
@@ -100,6 +101,7 @@ __host__ inline Layout make_layout(int num_seqs, int total_tokens, int hv, int d
     size_t o = 0;
     l.chunk_map = o; o = align256(o + (size_t)slots * 2 * 4);
     l.chunk_off = o; o = align256(o + (size_t)(num_seqs + 1) * 4);
+    l.seq_order = o; o = align256(o + (size_t)num_seqs * 4);
     l.W = o;   o = align256(o + per * C * dk * 2);
     l.Ut = o;  o = align256(o + per * C * dv * 2);
     l.M = o;   o = align256(o + per * C * C * 2);
@@ -113,6 +115,7 @@ __host__ inline Layout make_layout(int num_seqs, int total_tokens, int hv, int d
 struct Work {
     int2 *chunk_map;       // [slots] (seq, local chunk) or (-1, -1)
     int32_t *chunk_off;    // [N + 1] first chunk slot of each sequence
+    int32_t *seq_order;    // [N] sequences by decreasing length (state-kernel order)
     _Float16 *W, *Ut, *M, *QG, *KLt;
     float *GL;
     int slots;
@@ -154,6 +157,23 @@ __global__ __launch_bounds__(1024) void meta_kernel(const int32_t *cu, int n, Wo
     const int total = carry;
     if (tid == 0) w.chunk_off[n] = total;
     for (int s = total + tid; s < w.slots; s += 1024) w.chunk_map[s] = make_int2(-1, -1);
+
+    // Longest sequences first, so the state kernel's long sequential chains
+    // start in the first wave of workgroups (ties keep index order).  Counting
+    // ranks is O(N^2); beyond kOrderMax sequences the natural order is kept.
+    if (n <= kOrderMax) {
+        for (int s = tid; s < n; s += 1024) {
+            const int ls = cu[s + 1] - cu[s];
+            int rank = 0;
+            for (int m = 0; m < n; ++m) {
+                const int lm = cu[m + 1] - cu[m];
+                rank += (lm > ls) || (lm == ls && m < s);
+            }
+            w.seq_order[rank] = s;
+        }
+    } else {
+        for (int s = tid; s < n; s += 1024) w.seq_order[s] = s;
+    }
 }
 
 
@@ -191,7 +211,7 @@ __device__ __forceinline__ void wave_sync() {
 // ---------------------------------------------------------------------------
 constexpr int NTI = 512;   // threads of the intra kernel
 
-template <int DK, int DV> struct IntraSmem {
+template <int DK, int DV> struct IntraMain {
     union {
         struct {
             _Float16 Fk[C][DK + PADH];        // k * factor, every token
@@ -206,8 +226,21 @@ template <int DK, int DV> struct IntraSmem {
         _Float16 Vt[DV][C];                   // (beta V)^T, 16 B chunks XOR-swizzled by row
     } r3;
     float T[C][C + 1];                        // M during the levels, then T = (I + A)^-1
+};
+// Input tiles, staged once with 16-byte loads; they alias IntraMain, which is
+// not in use until the gate threads have copied them into registers.
+template <int DK> struct IntraInput {
+    float g[C][DK];
+    _Float16 k[C][DK];
+    _Float16 q[C][DK];
+};
+template <int DK, int DV> struct IntraSmem {
     float beta[C];
     float qtot[4][DK];                        // per-quarter gate products
+    union {
+        IntraMain<DK, DV> m;
+        IntraInput<DK> in;
+    } u;
 };
 
 __device__ __forceinline__ int vt_col(int j, int t) { return t ^ ((j & 7) << 3); }
@@ -247,11 +280,11 @@ __device__ __forceinline__ void factor_level(float (&P)[16], float (&S)[16], con
         const int t = 16 * qtr + tau;
         const float kv = (float)kr[tau >> 1][tau & 1];
         if (row_bit<LVL>(qtr, tau)) {
-            sm.r1.f.Fk[t][c] = (_Float16)(kv * P[tau]);
+            sm.u.m.r1.f.Fk[t][c] = (_Float16)(kv * P[tau]);
             const int ridx = ((t >> (LVL + 1)) << LVL) | (t & ((1 << LVL) - 1));
-            sm.r1.f.Fq[ridx][c] = (_Float16)((float)qr[tau >> 1][tau & 1] * P[tau]);
+            sm.u.m.r1.f.Fq[ridx][c] = (_Float16)((float)qr[tau >> 1][tau & 1] * P[tau]);
         } else {
-            sm.r1.f.Fk[t][c] = (_Float16)(kv * S[tau]);
+            sm.u.m.r1.f.Fk[t][c] = (_Float16)(kv * S[tau]);
         }
     }
     if constexpr (LVL == 4) sm.qtot[qtr][c] = P[15];   // quarter total (P over the whole quarter)
@@ -279,12 +312,12 @@ __device__ __forceinline__ void mfma_level(IntraSmem<DK, DV> &sm, int wave, int 
         ridx = rtok - 32;
         ctok = cbase + m;
     }
-    const _Float16 *arow = kind == 0 ? &sm.r1.f.Fk[rtok][0] : &sm.r1.f.Fq[ridx][0];
+    const _Float16 *arow = kind == 0 ? &sm.u.m.r1.f.Fk[rtok][0] : &sm.u.m.r1.f.Fq[ridx][0];
     f32x4 acc = zero4();
 #pragma unroll
     for (int kk = 0; kk < DK / 32; ++kk) {
         const int c8 = kk * 32 + kq * 8;
-        acc = mfma_f16(lds8(arow + c8), lds8(&sm.r1.f.Fk[ctok][c8]), acc);
+        acc = mfma_f16(lds8(arow + c8), lds8(&sm.u.m.r1.f.Fk[ctok][c8]), acc);
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -301,8 +334,8 @@ __device__ __forceinline__ void mfma_level(IntraSmem<DK, DV> &sm, int wave, int 
             valid = true;
         }
         if (valid) {
-            if (kind == 0) sm.r3.A[r][i] = sm.beta[r] * acc[jj];
-            else sm.T[r][i] = acc[jj];
+            if (kind == 0) sm.u.m.r3.A[r][i] = sm.beta[r] * acc[jj];
+            else sm.u.m.T[r][i] = acc[jj];
         }
     }
 }
@@ -326,7 +359,56 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     const IO *kg = reinterpret_cast<const IO *>(a.k);
     const IO *vg = reinterpret_cast<const IO *>(a.v);
 
-    // ---- phase 0: registers for the gate threads and the value threads ----
+    // ---- phase 0: stage g, k, q with 16-byte loads, then into gate-thread registers ----
+    {
+        constexpr int KV = 16 / sizeof(IO);   // io elements per 16-byte load
+        for (int e = tid; e < C * (DK / KV); e += NTI) {
+            const int r = e / (DK / KV), c0 = (e % (DK / KV)) * KV;
+            f16x8 kv8, qv8;
+            if (r < L) {
+                const size_t off = ((size_t)(t0 + r) * a.hk + hk) * DK + c0;
+                if constexpr (KV == 8) {
+                    kv8 = load8_f16<IO>(kg + off);
+                    qv8 = load8_f16<IO>(qg + off);
+                } else {
+                    const f32x4 x = load4(kg + off), y = load4(qg + off);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        kv8[u] = (_Float16)x[u];
+                        qv8[u] = (_Float16)y[u];
+                    }
+                }
+            } else {
+                kv8 = f16x8{};
+                qv8 = f16x8{};
+            }
+            if constexpr (KV == 8) {
+                *reinterpret_cast<f16x8 *>(&sm.u.in.k[r][c0]) = kv8;
+                *reinterpret_cast<f16x8 *>(&sm.u.in.q[r][c0]) = qv8;
+            } else {
+                f16x4 k4, q4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    k4[u] = kv8[u];
+                    q4[u] = qv8[u];
+                }
+                *reinterpret_cast<f16x4 *>(&sm.u.in.k[r][c0]) = k4;
+                *reinterpret_cast<f16x4 *>(&sm.u.in.q[r][c0]) = q4;
+            }
+        }
+        if constexpr (SCALAR) {
+            if (tid < C) sm.u.in.g[tid][0] = tid < L ? a.g[(size_t)(t0 + tid) * a.hv + h] : 0.f;
+        } else {
+            for (int e = tid; e < C * (DK / 4); e += NTI) {
+                const int r = e / (DK / 4), c0 = (e % (DK / 4)) * 4;
+                const f32x4 x = r < L ? *reinterpret_cast<const f32x4 *>(a.g + ((size_t)(t0 + r) * a.hv + h) * DK + c0)
+                                      : zero4();
+                *reinterpret_cast<f32x4 *>(&sm.u.in.g[r][c0]) = x;
+            }
+        }
+        if (tid < C) sm.beta[tid] = tid < L ? a.beta[(size_t)(t0 + tid) * a.hv + h] : 0.f;
+    }
+    __syncthreads();
     const bool fthread = tid < 4 * DK;
     const int fc = tid % DK, fq = tid / DK;      // channel, quarter
     float P[16], S[16];
@@ -335,25 +417,17 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 #pragma unroll
         for (int tau = 0; tau < 16; ++tau) {
             const int r = 16 * fq + tau;
-            float gv = 0.f, kv = 0.f, qv = 0.f;
-            if (r < L) {
-                const size_t t = t0 + r;
-                if constexpr (SCALAR) gv = a.g[t * a.hv + h];
-                else gv = a.g[(t * a.hv + h) * DK + fc];
-                kv = io_traits<IO>::load(kg, (t * a.hk + hk) * DK + fc);
-                qv = io_traits<IO>::load(qg, (t * a.hk + hk) * DK + fc);
-            }
-            P[tau] = exp_f(gv);
+            P[tau] = exp_f(SCALAR ? sm.u.in.g[r][0] : sm.u.in.g[r][fc]);
             S[tau] = 1.f;
-            kr[tau >> 1][tau & 1] = (_Float16)kv;
-            qr[tau >> 1][tau & 1] = (_Float16)qv;
+            kr[tau >> 1][tau & 1] = sm.u.in.k[r][fc];
+            qr[tau >> 1][tau & 1] = sm.u.in.q[r][fc];
         }
     }
-    if (tid < C) sm.beta[tid] = tid < L ? a.beta[(size_t)(t0 + tid) * a.hv + h] : 0.f;
+    __syncthreads();
     // A: the diagonal blocks' diagonal and upper triangle are zero
     for (int e = tid; e < 4 * 256; e += NTI) {
         const int b = e >> 8, rr = (e >> 4) & 15, ii = e & 15;
-        if (ii >= rr) sm.r3.A[16 * b + rr][16 * b + ii] = 0.f;
+        if (ii >= rr) sm.u.m.r3.A[16 * b + rr][16 * b + ii] = 0.f;
     }
     __syncthreads();
 
@@ -394,7 +468,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
             }
             d += __shfl_xor(d, 1, 64);
             d += __shfl_xor(d, 2, 64);
-            if (part == 0) sm.T[r][r] = d;
+            if (part == 0) sm.u.m.T[r][r] = d;
         }
         __syncthreads();
     }
@@ -415,9 +489,9 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
                 const float kv = (float)kr[tau >> 1][tau & 1], qv = (float)qr[tau >> 1][tau & 1];
                 kgv[e] = (_Float16)(sm.beta[t] * kv * gam);
                 klv[e] = (_Float16)(kv * rest);
-                sm.r1.stage[t][fc] = (_Float16)(qv * gam);
+                sm.u.m.r1.stage[t][fc] = (_Float16)(qv * gam);
             }
-            *reinterpret_cast<f16x8 *>(&sm.KGt[fc][16 * fq + 8 * g8]) = kgv;
+            *reinterpret_cast<f16x8 *>(&sm.u.m.KGt[fc][16 * fq + 8 * g8]) = kgv;
             // (K exp(G_last - G))^T in A-operand tile layout: rows c, k index t
             const int ln = (fc & 15) + 16 * (2 * (fq & 1) + g8);
             *reinterpret_cast<f16x8 *>(w.KLt + kl_off + ((size_t)((fc >> 4) * 2 + (fq >> 1)) * 64 + ln) * 8) = klv;
@@ -425,46 +499,48 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     }
     __syncthreads();
 
+    // ---- waves 4..7: 16-byte loads of the V tile, in flight during the stores and the inversion ----
+    constexpr int VKV = 16 / sizeof(IO);               // io elements per 16-byte load
+    constexpr int VPT = C * (DV / VKV) / (NTI / 2);    // loads per value thread
+    u32x4 vraw[VPT];
+    if (wave >= 4) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int e = (tid - NTI / 2) + i * (NTI / 2);
+            const int r = e / (DV / VKV), c0 = (e % (DV / VKV)) * VKV;
+            vraw[i] = r < L ? *reinterpret_cast<const u32x4 *>(vg + ((size_t)(t0 + r) * a.hv + h) * DV + c0)
+                            : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
     // ---- A-operand tile stores: Q exp(G) and M (lower triangle incl. diagonal) ----
     for (int e = tid; e < (C / 16) * (DK / 32) * 64; e += NTI) {
         const int tile = e >> 6, l = e & 63;
         const int rt = tile / (DK / 32), kk = tile % (DK / 32);
         *reinterpret_cast<f16x8 *>(w.QG + qg_off + (size_t)e * 8) =
-            lds8(&sm.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]);
+            lds8(&sm.u.m.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]);
     }
     for (int e = tid; e < (C / 16) * (C / 32) * 64; e += NTI) {
         const int tile = e >> 6, l = e & 63;
         const int r = 16 * (tile >> 1) + (l & 15), i0 = 32 * (tile & 1) + 8 * (l >> 4);
         f16x8 v;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (_Float16)(i0 + u <= r ? sm.T[r][i0 + u] : 0.f);
+        for (int u = 0; u < 8; ++u) v[u] = (_Float16)(i0 + u <= r ? sm.u.m.T[r][i0 + u] : 0.f);
         *reinterpret_cast<f16x8 *>(w.M + sh * C * C + (size_t)e * 8) = v;
     }
     __syncthreads();
     // the blocks of T above the block diagonal are zero
     for (int e = tid; e < C * C; e += NTI) {
         const int r = e / C, i = e % C;
-        if ((i >> 4) > (r >> 4)) sm.T[r][i] = 0.f;
+        if ((i >> 4) > (r >> 4)) sm.u.m.T[r][i] = 0.f;
     }
 
-    // ---- T = (I + A)^-1 (blocked, fp32 MFMA, waves 0..3); waves 4..7 load V ----
-    constexpr int TPJ = (NTI / 2) / DV;   // value threads per value column (waves 4..7)
-    constexpr int TOKV = C / TPJ;         // tokens per value thread
-    const int vt_id = tid - NTI / 2;
-    const int vj = vt_id % DV, vpart = vt_id / DV;
-    _Float16 vr[TOKV];
-    if (wave >= 4) {
-#pragma unroll
-        for (int i = 0; i < TOKV; ++i) {
-            const int r = vpart * TOKV + i;
-            vr[i] = (_Float16)(r < L ? io_traits<IO>::load(vg, ((size_t)(t0 + r) * a.hv + h) * DV + vj) : 0.f);
-        }
-    }
+    // ---- T = (I + A)^-1 (blocked, fp32 MFMA, waves 0..3) ----
     constexpr int LD = C + 1;
     if (wave < 4) {
-        float *scr = &sm.r1.scr[wave][0][0];
+        float *scr = &sm.u.m.r1.scr[wave][0][0];
         const int b = wave;
-        const float *Ab = &sm.r3.A[16 * b][16 * b];
+        const float *Ab = &sm.u.m.r3.A[16 * b][16 * b];
         float *A2 = scr, *A4 = scr + 256, *X = scr + 512;
         // (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) for strictly lower A
         f32x4 v = mm16(Ab, LD, Ab, LD, lane);
@@ -494,26 +570,26 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         t = mm16(X, 16, A2, 16, lane);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) xv[jj] += t[jj];
-        st16(&sm.T[16 * b][16 * b], LD, xv, lane);
+        st16(&sm.u.m.T[16 * b][16 * b], LD, xv, lane);
     }
     __syncthreads();
     // off-diagonal blocks by distance d: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
     for (int d = 1; d <= 3; ++d) {
         if (wave < 4 - d) {
-            float *X = &sm.r1.scr[wave][0][0];
+            float *X = &sm.u.m.r1.scr[wave][0][0];
             const int b = wave, aa = b + d;
             f32x4 acc = zero4();
             for (int c = b; c < aa; ++c) {
-                const f32x4 t = mm16(&sm.r3.A[16 * aa][16 * c], LD, &sm.T[16 * c][16 * b], LD, lane);
+                const f32x4 t = mm16(&sm.u.m.r3.A[16 * aa][16 * c], LD, &sm.u.m.T[16 * c][16 * b], LD, lane);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) acc[jj] += t[jj];
             }
             st16(X, 16, acc, lane);
             wave_sync();
-            f32x4 tv = mm16(&sm.T[16 * aa][16 * aa], LD, X, 16, lane);
+            f32x4 tv = mm16(&sm.u.m.T[16 * aa][16 * aa], LD, X, 16, lane);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) tv[jj] = -tv[jj];
-            st16(&sm.T[16 * aa][16 * b], LD, tv, lane);
+            st16(&sm.u.m.T[16 * aa][16 * b], LD, tv, lane);
         }
         __syncthreads();
     }
@@ -521,9 +597,18 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     // ---- (beta V)^T into the (now free) A region ----
     if (wave >= 4) {
 #pragma unroll
-        for (int i = 0; i < TOKV; ++i) {
-            const int r = vpart * TOKV + i;
-            sm.r3.Vt[vj][vt_col(vj, r)] = (_Float16)(sm.beta[r] * (float)vr[i]);
+        for (int i = 0; i < VPT; ++i) {
+            const int e = (tid - NTI / 2) + i * (NTI / 2);
+            const int r = e / (DV / VKV), c0 = (e % (DV / VKV)) * VKV;
+            const float b = sm.beta[r];
+#pragma unroll
+            for (int u = 0; u < VKV; ++u) {
+                float x;
+                if constexpr (VKV == 8) x = __uint_as_float(u & 1 ? (vraw[i][u >> 1] & 0xffff0000u) : (vraw[i][u >> 1] << 16));
+                else x = __uint_as_float(vraw[i][u]);
+                const int j = c0 + u;
+                sm.u.m.r3.Vt[j][vt_col(j, r)] = (_Float16)(b * x);
+            }
         }
     }
     __syncthreads();
@@ -535,7 +620,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         f16x8 ta[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const float *tp = &sm.T[16 * rt + m][kk * 32 + kq * 8];
+            const float *tp = &sm.u.m.T[16 * rt + m][kk * 32 + kq * 8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) ta[kk][e] = (_Float16)tp[e];
         }
@@ -543,18 +628,18 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         if (which == 0) {
 #pragma unroll
             for (int ct = 0; ct < DK / 16; ++ct) {
-                f32x4 acc = mfma_f16(ta[0], lds8(&sm.KGt[16 * ct + m][kq * 8]), zero4());
-                if (k1) acc = mfma_f16(ta[1], lds8(&sm.KGt[16 * ct + m][32 + kq * 8]), acc);
+                f32x4 acc = mfma_f16(ta[0], lds8(&sm.u.m.KGt[16 * ct + m][kq * 8]), zero4());
+                if (k1) acc = mfma_f16(ta[1], lds8(&sm.u.m.KGt[16 * ct + m][32 + kq * 8]), acc);
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) sm.r1.stage[16 * rt + 4 * kq + jj][16 * ct + m] = (_Float16)acc[jj];
+                for (int jj = 0; jj < 4; ++jj) sm.u.m.r1.stage[16 * rt + 4 * kq + jj][16 * ct + m] = (_Float16)acc[jj];
             }
         } else {
             _Float16 *Ug = w.Ut + sh * C * DV;
 #pragma unroll
             for (int ct = 0; ct < DV / 16; ++ct) {
                 const int j = 16 * ct + m;
-                f32x4 acc = mfma_f16(ta[0], lds8(&sm.r3.Vt[j][vt_col(j, kq * 8)]), zero4());
-                if (k1) acc = mfma_f16(ta[1], lds8(&sm.r3.Vt[j][vt_col(j, 32 + kq * 8)]), acc);
+                f32x4 acc = mfma_f16(ta[0], lds8(&sm.u.m.r3.Vt[j][vt_col(j, kq * 8)]), zero4());
+                if (k1) acc = mfma_f16(ta[1], lds8(&sm.u.m.r3.Vt[j][vt_col(j, 32 + kq * 8)]), acc);
                 f16x4 h4;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) h4[jj] = (_Float16)acc[jj];
@@ -569,7 +654,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
             const int tile = e >> 6, l = e & 63;
             const int rt = tile / (DK / 32), kk = tile % (DK / 32);
             *reinterpret_cast<f16x8 *>(Wg + (size_t)e * 8) =
-                lds8(&sm.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]);
+                lds8(&sm.u.m.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]);
         }
     }
 }
@@ -584,10 +669,25 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 //     X[16 rt + 4 (l / 16) + jj][16 ct + l % 16], jj = 0..3  (8 B per lane)
 // so every operand load is one contiguous 16 B (or 8 B) access per lane.
 // ---------------------------------------------------------------------------
-template <int DK, int BV> struct StateSmem {
+template <int DK, int BV, typename IO> struct StateSmem {
     _Float16 Sh[BV][DK + PADH];   // S^T as fp16 (B operand of W S and QG S)
     _Float16 Vn[BV][C + PADH];    // U^T as fp16 (B operand of M U and KLt U)
+    IO Ost[4][16][BV + 16 / sizeof(IO)];   // per-wave output rows, for 16-byte stores
 };
+
+// Workgroup -> (value tile, head, sequence rank).  Consecutive workgroup ids
+// go to different XCDs (round robin over kXcd); the value tiles of one
+// (sequence, head) are given ids kXcd apart so they share an XCD's L2 and the
+// second tile's operand reads hit it.  Rank-major: longest sequences first.
+constexpr int kXcd = 8;
+template <int NVT>
+__device__ __forceinline__ void state_unit(int id, int hv, int &vt, int &h, int &rank) {
+    const int xcd = id % kXcd, slot = id / kXcd;
+    vt = slot % NVT;
+    const int unit = (slot / NVT) * kXcd + xcd;     // (head, rank) pair index
+    h = unit % hv;
+    rank = unit / hv;
+}
 
 template <typename ST> __device__ __forceinline__ f32x4 load_state4(const ST *p);
 template <> __device__ __forceinline__ f32x4 load_state4<float>(const float *p) {
@@ -607,7 +707,7 @@ __device__ __forceinline__ f16x4 gld4(const _Float16 *p) { return *reinterpret_c
 
 template <int DK, int DV, int BV, typename IO, typename ST>
 __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
-    __shared__ __align__(16) StateSmem<DK, BV> sm;
+    __shared__ __align__(16) StateSmem<DK, BV, IO> sm;
     constexpr int KK = DK / 32;          // k-steps over key channels
     constexpr int CT = BV / 16;          // value column tiles of this workgroup
     constexpr int R = DK / 16;           // key row tiles of the state
@@ -616,7 +716,10 @@ __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
     constexpr int CTW = CT / WPR;             // state column tiles per wave
     static_assert(CTW >= 1, "tile");
 
-    const int vt = blockIdx.x, n = blockIdx.y, h = blockIdx.z;
+    int vt, h, rank;
+    state_unit<DV / BV>(blockIdx.x, a.hv, vt, h, rank);
+    if (rank >= a.num_seqs) return;   // padding of the last XCD round
+    const int n = w.seq_order[rank];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, kq = lane >> 4;
     const int j0 = vt * BV;
@@ -647,35 +750,48 @@ __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
                           : zero4();
 
     IO *og = reinterpret_cast<IO *>(a.o);
-    for (int ch = 0; ch < nchunks; ++ch) {
+    // Operands of one chunk for this wave (row tile `wave` of the chunk's
+    // tokens; the wave's state row tiles for KLt).  The next chunk's operands
+    // are loaded while the current chunk computes.
+    struct Ops {
+        f16x8 Wa[KK], Qa[KK], Ma[2], Ka[RPW][2];
+        f16x4 Ua[CT];
+        f32x4 gl[RPW];
+    };
+    auto load_ops = [&](int ch, Ops &op) {
         const size_t sh = (size_t)(s0 + ch) * a.hv + h;
-        const int t0 = tbeg + ch * C;
-        const int L = min(C, tend - t0);
-        // operands of this wave (row tile `wave` of the chunk's tokens)
         const _Float16 *Wg = w.W + sh * C * DK + (size_t)wave * KK * 512 + lane * 8;
         const _Float16 *Qg = w.QG + sh * C * DK + (size_t)wave * KK * 512 + lane * 8;
         const _Float16 *Mg = w.M + sh * C * C + (size_t)wave * 2 * 512 + lane * 8;
         const _Float16 *Ug = w.Ut + sh * C * DV + ((size_t)wave * (DV / 16) + vt * CT) * 256 + lane * 4;
         const _Float16 *Kg = w.KLt + sh * DK * C + lane * 8;
         const float *GLg = w.GL + sh * DK;
-        f16x8 Wa[KK], Qa[KK], Ma[2], Ka[RPW][2];
-        f16x4 Ua[CT];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            Wa[kk] = gld8(Wg + kk * 512);
-            Qa[kk] = gld8(Qg + kk * 512);
+            op.Wa[kk] = gld8(Wg + kk * 512);
+            op.Qa[kk] = gld8(Qg + kk * 512);
         }
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) Ua[ct] = gld4(Ug + ct * 256);
+        for (int ct = 0; ct < CT; ++ct) op.Ua[ct] = gld4(Ug + ct * 256);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) Ma[kk] = gld8(Mg + kk * 512);
+        for (int kk = 0; kk < 2; ++kk) op.Ma[kk] = gld8(Mg + kk * 512);
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) Ka[r][kk] = gld8(Kg + ((size_t)(rt0 + r) * 2 + kk) * 512);
-        f32x4 gl[RPW];
+            for (int kk = 0; kk < 2; ++kk) op.Ka[r][kk] = gld8(Kg + ((size_t)(rt0 + r) * 2 + kk) * 512);
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) gl[r] = *reinterpret_cast<const f32x4 *>(GLg + 16 * (rt0 + r) + 4 * kq);
+        for (int r = 0; r < RPW; ++r) op.gl[r] = *reinterpret_cast<const f32x4 *>(GLg + 16 * (rt0 + r) + 4 * kq);
+    };
+    Ops cur, nxt;
+    if (nchunks > 0) load_ops(0, cur);
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int t0 = tbeg + ch * C;
+        const int L = min(C, tend - t0);
+        if (ch + 1 < nchunks) load_ops(ch + 1, nxt);
+        const f16x8 *Wa = cur.Wa, *Qa = cur.Qa, *Ma = cur.Ma;
+        const f16x4 *Ua = cur.Ua;
+        const f32x4 *gl = cur.gl;
+        auto &Ka = cur.Ka;
 
         // (a) S^T -> fp16 LDS
 #pragma unroll
@@ -713,11 +829,20 @@ __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
             for (int kk = 0; kk < 2; ++kk)
                 Oacc[ct] = mfma_f16(Ma[kk], lds8(&sm.Vn[16 * ct + m][kk * 32 + kq * 8]), Oacc[ct]);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 16 * wave + 4 * kq + jj;
+            for (int jj = 0; jj < 4; ++jj)
+                io_traits<IO>::store(&sm.Ost[wave][4 * kq + jj][0], 16 * ct + m, a.scale * Oacc[ct][jj]);
+        }
+        wave_sync();
+        {
+            // 16 rows x BV values of this wave -> 16-byte stores of the valid rows
+            constexpr int EPV = 16 / sizeof(IO), VPR = BV / EPV;   // elements per vector, vectors per row
+#pragma unroll
+            for (int e = lane; e < 16 * VPR; e += 64) {
+                const int rr = e / VPR, c0 = (e % VPR) * EPV;
+                const int r = 16 * wave + rr;
                 if (r < L)
-                    io_traits<IO>::store(og, ((size_t)(t0 + r) * a.hv + h) * DV + j0 + 16 * ct + m,
-                                         a.scale * Oacc[ct][jj]);
+                    *reinterpret_cast<u32x4 *>(og + ((size_t)(t0 + r) * a.hv + h) * DV + j0 + c0) =
+                        *reinterpret_cast<const u32x4 *>(&sm.Ost[wave][rr][c0]);
             }
         }
         // (d) S = diag(exp G_last) S + KLt U
@@ -731,6 +856,7 @@ __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
                 for (int kk = 0; kk < 2; ++kk)
                     S[r][c] = mfma_f16(Ka[r][kk], lds8(&sm.Vn[16 * (ct0 + c) + m][kk * 32 + kq * 8]), S[r][c]);
             }
+        cur = nxt;
     }
 
     if (row_out >= 0) {
@@ -764,7 +890,10 @@ hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
 
 template <int DK, int DV, int BV, typename IO>
 hipError_t launch_state_bv(PrefillArgs &a, Work &w, hipStream_t s) {
-    dim3 grid(DV / BV, a.num_seqs, a.hv);
+    // 1-D grid over (value tile, head, sequence rank); see state_unit
+    const long units = (long)a.hv * a.num_seqs;
+    const long padded = (units + kXcd - 1) / kXcd * kXcd;
+    dim3 grid((unsigned)(padded * (DV / BV)));
     if (a.state_bf16) state_kernel<DK, DV, BV, IO, bf16><<<grid, NT, 0, s>>>(a, w);
     else state_kernel<DK, DV, BV, IO, float><<<grid, NT, 0, s>>>(a, w);
     return hipGetLastError();
@@ -814,6 +943,7 @@ hipError_t launch_prefill(PrefillArgs &a, void *workspace, hipStream_t stream) {
     Work w;
     w.chunk_map = reinterpret_cast<int2 *>(base + l.chunk_map);
     w.chunk_off = reinterpret_cast<int32_t *>(base + l.chunk_off);
+    w.seq_order = reinterpret_cast<int32_t *>(base + l.seq_order);
     w.W = reinterpret_cast<_Float16 *>(base + l.W);
     w.Ut = reinterpret_cast<_Float16 *>(base + l.Ut);
     w.M = reinterpret_cast<_Float16 *>(base + l.M);
