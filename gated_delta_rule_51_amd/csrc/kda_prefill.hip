@@ -275,16 +275,25 @@ __device__ __forceinline__ void factor_level(float (&P)[16], float (&S)[16], con
             for (int tau = 0; tau < 16; ++tau) P[tau] *= tot;
         }
     }
+    // Operand rows for token pairs (tau, tau + 1) with packed fp16 products.
 #pragma unroll
-    for (int tau = 0; tau < 16; ++tau) {
-        const int t = 16 * qtr + tau;
-        const float kv = (float)kr[tau >> 1][tau & 1];
-        if (row_bit<LVL>(qtr, tau)) {
-            sm.u.m.r1.f.Fk[t][c] = (_Float16)(kv * P[tau]);
-            const int ridx = ((t >> (LVL + 1)) << LVL) | (t & ((1 << LVL) - 1));
-            sm.u.m.r1.f.Fq[ridx][c] = (_Float16)((float)qr[tau >> 1][tau & 1] * P[tau]);
-        } else {
-            sm.u.m.r1.f.Fk[t][c] = (_Float16)(kv * S[tau]);
+    for (int p2 = 0; p2 < 8; ++p2) {
+        const int ta = 2 * p2, tb = ta + 1;
+        const int t = 16 * qtr + ta;
+        const bool ra = row_bit<LVL>(qtr, ta), rb = row_bit<LVL>(qtr, tb);
+        const f16x2 fac = {(_Float16)(ra ? P[ta] : S[ta]), (_Float16)(rb ? P[tb] : S[tb])};
+        const f16x2 fk = kr[p2] * fac;
+        sm.u.m.r1.f.Fk[t][c] = fk[0];
+        sm.u.m.r1.f.Fk[t + 1][c] = fk[1];
+        if constexpr (LVL >= 1) {
+            if (ra) {   // at LVL >= 1 the two tokens of a pair share their role
+                const f16x2 fq = qr[p2] * fac;
+                const int ridx = ((t >> (LVL + 1)) << LVL) | (t & ((1 << LVL) - 1));
+                sm.u.m.r1.f.Fq[ridx][c] = fq[0];
+                sm.u.m.r1.f.Fq[ridx + 1][c] = fq[1];
+            }
+        } else {        // level 0: only the odd token of a pair is a row
+            sm.u.m.r1.f.Fq[(t + 1) >> 1][c] = qr[p2][1] * fac[1];
         }
     }
     if constexpr (LVL == 4) sm.qtot[qtr][c] = P[15];   // quarter total (P over the whole quarter)
