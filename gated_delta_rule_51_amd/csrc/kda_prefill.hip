@@ -236,7 +236,6 @@ template <int DK> struct IntraInput {
 };
 template <int DK, int DV> struct IntraSmem {
     float beta[C];
-    float qtot[4][DK];                        // per-quarter gate products
     union {
         IntraMain<DK, DV> m;
         IntraInput<DK> in;
@@ -245,58 +244,92 @@ template <int DK, int DV> struct IntraSmem {
 
 __device__ __forceinline__ int vt_col(int j, int t) { return t ^ ((j & 7) << 3); }
 
-template <int LVL> __device__ __forceinline__ bool row_bit(int qtr, int tau) {
-    if constexpr (LVL < 4) return (tau >> LVL) & 1;
-    else if constexpr (LVL == 4) return qtr & 1;
-    else return (qtr >> 1) & 1;
+// Gate threads: thread = (channel pair cp: channels 2cp, 2cp+1; eighth e8:
+// tokens t = 8 e8 + tau, tau = 0..7).  Token bit LVL says whether t is a row
+// (later half) or a column at level LVL.
+template <int LVL> __device__ __forceinline__ bool row_bit(int e8, int tau) {
+    if constexpr (LVL < 3) return (tau >> LVL) & 1;
+    else return (e8 >> (LVL - 3)) & 1;
 }
 
-// Advance the chains from level LVL-1 to LVL and write this level's operand rows.
+// Per-eighth gate totals exchanged during the levels (KGt is unused until the
+// chunk-level phase, so its space holds them).
+template <int DK, int DV> __device__ __forceinline__ float (*eighth_totals(IntraSmem<DK, DV> &sm))[DK] {
+    return reinterpret_cast<float (*)[DK]>(&sm.u.m.KGt[0][0]);
+}
+
+// Advance the chains from level LVL-1 to LVL and write this level's operand
+// rows: P[tau] / S[tau] hold (channel 2cp, channel 2cp+1) products as float2.
 template <int LVL, int DK, int DV>
-__device__ __forceinline__ void factor_level(float (&P)[16], float (&S)[16], const f16x2 (&kr)[8],
-                                             const f16x2 (&qr)[8], IntraSmem<DK, DV> &sm, int c, int qtr) {
-    if constexpr (LVL >= 1 && LVL <= 4) {
+__device__ __forceinline__ void factor_level(f32x2 (&P)[8], f32x2 (&S)[8], const f16x2 (&kr)[8],
+                                             const f16x2 (&qr)[8], IntraSmem<DK, DV> &sm, int cp, int e8,
+                                             f32x2 &H0, f32x2 &H1) {
+    float (*etot)[DK] = eighth_totals(sm);
+    if constexpr (LVL >= 1 && LVL <= 3) {
         constexpr int hb = 1 << (LVL - 1);
 #pragma unroll
-        for (int tau = 0; tau < 16; ++tau)   // S first: it reads P of level LVL-1
+        for (int tau = 0; tau < 8; ++tau)   // S first: it reads P of level LVL-1
             if (((tau >> (LVL - 1)) & 1) == 0) S[tau] *= P[tau | (2 * hb - 1)];
 #pragma unroll
-        for (int tau = 15; tau >= 0; --tau)
+        for (int tau = 7; tau >= 0; --tau)
             if ((tau >> (LVL - 1)) & 1) P[tau] *= P[(tau & ~(2 * hb - 1)) + hb - 1];
-    } else if constexpr (LVL == 5) {
-        // blocks of 32 tokens span two quarters: use the partner quarter's total
-        if ((qtr & 1) == 0) {
-            const float tot = sm.qtot[qtr + 1][c];
+    } else if constexpr (LVL == 4) {
+        // 16-token blocks = eighths (2j, 2j+1): the partner eighth's total
+        const int pe = e8 ^ 1;
+        const f32x2 tot = {etot[pe][2 * cp], etot[pe][2 * cp + 1]};
+        if ((e8 & 1) == 0) {
 #pragma unroll
-            for (int tau = 0; tau < 16; ++tau) S[tau] *= tot;
+            for (int tau = 0; tau < 8; ++tau) S[tau] *= tot;
         } else {
-            const float tot = sm.qtot[qtr - 1][c];
 #pragma unroll
-            for (int tau = 0; tau < 16; ++tau) P[tau] *= tot;
+            for (int tau = 0; tau < 8; ++tau) P[tau] *= tot;
+        }
+    } else if constexpr (LVL == 5) {
+        // 32-token blocks = eighths 4j..4j+3: the partner 16-token block's total
+        f32x2 et[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) et[e] = f32x2{etot[e][2 * cp], etot[e][2 * cp + 1]};
+        H0 = et[0] * et[1] * et[2] * et[3];
+        H1 = et[4] * et[5] * et[6] * et[7];
+        f32x2 tot;   // total of the other 16-token block of this half
+        if ((e8 & 4) == 0) tot = (e8 & 2) ? et[0] * et[1] : et[2] * et[3];
+        else tot = (e8 & 2) ? et[4] * et[5] : et[6] * et[7];
+        if ((e8 & 2) == 0) {
+#pragma unroll
+            for (int tau = 0; tau < 8; ++tau) S[tau] *= tot;
+        } else {
+#pragma unroll
+            for (int tau = 0; tau < 8; ++tau) P[tau] *= tot;
         }
     }
-    // Operand rows for token pairs (tau, tau + 1) with packed fp16 products.
+    // operand rows: two channels per 4-byte write.  The row/column role is
+    // compile-time for LVL < 3 and uniform per thread otherwise.
+    auto emit = [&](int tau, bool row, const f32x2 f) {
+        const int t = 8 * e8 + tau;
+        const f16x2 fac = {(_Float16)f[0], (_Float16)f[1]};
+        *reinterpret_cast<f16x2 *>(&sm.u.m.r1.f.Fk[t][2 * cp]) = kr[tau] * fac;
+        if (row) {
+            const int ridx = ((t >> (LVL + 1)) << LVL) | (t & ((1 << LVL) - 1));
+            *reinterpret_cast<f16x2 *>(&sm.u.m.r1.f.Fq[ridx][2 * cp]) = qr[tau] * fac;
+        }
+    };
+    if constexpr (LVL < 3) {
 #pragma unroll
-    for (int p2 = 0; p2 < 8; ++p2) {
-        const int ta = 2 * p2, tb = ta + 1;
-        const int t = 16 * qtr + ta;
-        const bool ra = row_bit<LVL>(qtr, ta), rb = row_bit<LVL>(qtr, tb);
-        const f16x2 fac = {(_Float16)(ra ? P[ta] : S[ta]), (_Float16)(rb ? P[tb] : S[tb])};
-        const f16x2 fk = kr[p2] * fac;
-        sm.u.m.r1.f.Fk[t][c] = fk[0];
-        sm.u.m.r1.f.Fk[t + 1][c] = fk[1];
-        if constexpr (LVL >= 1) {
-            if (ra) {   // at LVL >= 1 the two tokens of a pair share their role
-                const f16x2 fq = qr[p2] * fac;
-                const int ridx = ((t >> (LVL + 1)) << LVL) | (t & ((1 << LVL) - 1));
-                sm.u.m.r1.f.Fq[ridx][c] = fq[0];
-                sm.u.m.r1.f.Fq[ridx + 1][c] = fq[1];
-            }
-        } else {        // level 0: only the odd token of a pair is a row
-            sm.u.m.r1.f.Fq[(t + 1) >> 1][c] = qr[p2][1] * fac[1];
+        for (int tau = 0; tau < 8; ++tau) {
+            if ((tau >> LVL) & 1) emit(tau, true, P[tau]);
+            else emit(tau, false, S[tau]);
+        }
+    } else {
+        if (row_bit<LVL>(e8, 0)) {
+#pragma unroll
+            for (int tau = 0; tau < 8; ++tau) emit(tau, true, P[tau]);
+        } else {
+#pragma unroll
+            for (int tau = 0; tau < 8; ++tau) emit(tau, false, S[tau]);
         }
     }
-    if constexpr (LVL == 4) sm.qtot[qtr][c] = P[15];   // quarter total (P over the whole quarter)
+    if constexpr (LVL == 3)   // eighth total (P over the whole eighth), read at levels 4 and 5
+        *reinterpret_cast<f32x2 *>(&etot[e8][2 * cp]) = P[7];
 }
 
 // MFMA tiles of level LVL: A (kind 0) and M (kind 1); valid pairs scattered to LDS.
@@ -419,17 +452,23 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     }
     __syncthreads();
     const bool fthread = tid < 4 * DK;
-    const int fc = tid % DK, fq = tid / DK;      // channel, quarter
-    float P[16], S[16];
-    f16x2 kr[8], qr[8];   // k, q rounded to fp16 (exact for bf16 inputs in range)
+    const int cp = tid % (DK / 2), e8 = tid / (DK / 2);   // channel pair, eighth (if fthread)
+    f32x2 P[8], S[8], H0, H1;
+    f16x2 kr[8], qr[8];   // k, q of channels (2cp, 2cp+1), rounded to fp16 (exact for bf16 in range)
     if (fthread) {
 #pragma unroll
-        for (int tau = 0; tau < 16; ++tau) {
-            const int r = 16 * fq + tau;
-            P[tau] = exp_f(SCALAR ? sm.u.in.g[r][0] : sm.u.in.g[r][fc]);
-            S[tau] = 1.f;
-            kr[tau >> 1][tau & 1] = sm.u.in.k[r][fc];
-            qr[tau >> 1][tau & 1] = sm.u.in.q[r][fc];
+        for (int tau = 0; tau < 8; ++tau) {
+            const int r = 8 * e8 + tau;
+            if constexpr (SCALAR) {
+                const float d = exp_f(sm.u.in.g[r][0]);
+                P[tau] = f32x2{d, d};
+            } else {
+                const f32x2 gv = *reinterpret_cast<const f32x2 *>(&sm.u.in.g[r][2 * cp]);
+                P[tau] = f32x2{exp_f(gv[0]), exp_f(gv[1])};
+            }
+            S[tau] = f32x2{1.f, 1.f};
+            kr[tau] = *reinterpret_cast<const f16x2 *>(&sm.u.in.k[r][2 * cp]);
+            qr[tau] = *reinterpret_cast<const f16x2 *>(&sm.u.in.q[r][2 * cp]);
         }
     }
     __syncthreads();
@@ -445,12 +484,12 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     for (int lvl = 0; lvl < 6; ++lvl) {
         if (fthread) {
             switch (lvl) {
-            case 0: factor_level<0>(P, S, kr, qr, sm, fc, fq); break;
-            case 1: factor_level<1>(P, S, kr, qr, sm, fc, fq); break;
-            case 2: factor_level<2>(P, S, kr, qr, sm, fc, fq); break;
-            case 3: factor_level<3>(P, S, kr, qr, sm, fc, fq); break;
-            case 4: factor_level<4>(P, S, kr, qr, sm, fc, fq); break;
-            default: factor_level<5>(P, S, kr, qr, sm, fc, fq); break;
+            case 0: factor_level<0>(P, S, kr, qr, sm, cp, e8, H0, H1); break;
+            case 1: factor_level<1>(P, S, kr, qr, sm, cp, e8, H0, H1); break;
+            case 2: factor_level<2>(P, S, kr, qr, sm, cp, e8, H0, H1); break;
+            case 3: factor_level<3>(P, S, kr, qr, sm, cp, e8, H0, H1); break;
+            case 4: factor_level<4>(P, S, kr, qr, sm, cp, e8, H0, H1); break;
+            default: factor_level<5>(P, S, kr, qr, sm, cp, e8, H0, H1); break;
             }
         }
         __syncthreads();
@@ -485,25 +524,36 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     // ---- chunk-level factors: exp(G_t), exp(G_last - G_t) ----
     const size_t qg_off = sh * C * DK, kl_off = sh * DK * C;
     if (fthread) {
-        const float h0t = sm.qtot[0][fc] * sm.qtot[1][fc], h1t = sm.qtot[2][fc] * sm.qtot[3][fc];
-        if (fq == 0) w.GL[sh * DK + fc] = h0t * h1t;
+        if (e8 == 0) {
+            const f32x2 gl = H0 * H1;
+            w.GL[sh * DK + 2 * cp] = gl[0];
+            w.GL[sh * DK + 2 * cp + 1] = gl[1];
+        }
+        f16x8 kg0, kg1, kl0, kl1;   // channels 2cp and 2cp+1, tokens 8 e8 .. 8 e8 + 7
 #pragma unroll
-        for (int g8 = 0; g8 < 2; ++g8) {
-            f16x8 kgv, klv;
+        for (int tau = 0; tau < 8; ++tau) {
+            const int t = 8 * e8 + tau;
+            const f32x2 gam = e8 >= 4 ? P[tau] * H0 : P[tau];     // exp(G_t)
+            const f32x2 rest = e8 < 4 ? S[tau] * H1 : S[tau];     // exp(G_last - G_t)
+            const float b = sm.beta[t];
+            const float k0 = (float)kr[tau][0], k1 = (float)kr[tau][1];
+            kg0[tau] = (_Float16)(b * k0 * gam[0]);
+            kg1[tau] = (_Float16)(b * k1 * gam[1]);
+            kl0[tau] = (_Float16)(k0 * rest[0]);
+            kl1[tau] = (_Float16)(k1 * rest[1]);
+            const f16x2 qgam = {(_Float16)((float)qr[tau][0] * gam[0]), (_Float16)((float)qr[tau][1] * gam[1])};
+            *reinterpret_cast<f16x2 *>(&sm.u.m.r1.stage[t][2 * cp]) = qgam;
+        }
+        // (the eighth totals held in the KGt space were last read at level 5)
+        *reinterpret_cast<f16x8 *>(&sm.u.m.KGt[2 * cp][8 * e8]) = kg0;
+        *reinterpret_cast<f16x8 *>(&sm.u.m.KGt[2 * cp + 1][8 * e8]) = kg1;
+        // (K exp(G_last - G))^T in A-operand tile layout: rows c, k index t
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tau = 8 * g8 + e, t = 16 * fq + tau;
-                const float gam = fq >= 2 ? P[tau] * h0t : P[tau];        // exp(G_t)
-                const float rest = fq < 2 ? S[tau] * h1t : S[tau];        // exp(G_last - G_t)
-                const float kv = (float)kr[tau >> 1][tau & 1], qv = (float)qr[tau >> 1][tau & 1];
-                kgv[e] = (_Float16)(sm.beta[t] * kv * gam);
-                klv[e] = (_Float16)(kv * rest);
-                sm.u.m.r1.stage[t][fc] = (_Float16)(qv * gam);
-            }
-            *reinterpret_cast<f16x8 *>(&sm.u.m.KGt[fc][16 * fq + 8 * g8]) = kgv;
-            // (K exp(G_last - G))^T in A-operand tile layout: rows c, k index t
-            const int ln = (fc & 15) + 16 * (2 * (fq & 1) + g8);
-            *reinterpret_cast<f16x8 *>(w.KLt + kl_off + ((size_t)((fc >> 4) * 2 + (fq >> 1)) * 64 + ln) * 8) = klv;
+        for (int u = 0; u < 2; ++u) {
+            const int c = 2 * cp + u;
+            const int ln = (c & 15) + 16 * (e8 & 3);
+            *reinterpret_cast<f16x8 *>(w.KLt + kl_off + ((size_t)((c >> 4) * 2 + (e8 >> 2)) * 64 + ln) * 8) =
+                u ? kl1 : kl0;
         }
     }
     __syncthreads();
