@@ -236,13 +236,19 @@ template <int DK> struct IntraInput {
 };
 template <int DK, int DV> struct IntraSmem {
     float beta[C];
+    float mdiag[C];   // q_t . k_t, the diagonal of M
     union {
         IntraMain<DK, DV> m;
         IntraInput<DK> in;
     } u;
 };
 
-__device__ __forceinline__ int vt_col(int j, int t) { return t ^ ((j & 7) << 3); }
+// Column of token t in row j of Vt: the 16-byte group is XORed with
+// (j ^ j/8) mod 8.  The MFMA B-operand reads (8 consecutive rows j, one group
+// each) and the transposing writes (a wave holds 16 channel groups of 8 and
+// 4 tokens, one channel offset j mod 8 per instruction) then spread over the
+// banks.
+__device__ __forceinline__ int vt_col(int j, int t) { return t ^ (((j ^ (j >> 3)) & 7) << 3); }
 
 // Gate threads: thread = (channel pair cp: channels 2cp, 2cp+1; eighth e8:
 // tokens t = 8 e8 + tau, tau = 0..7).  Token bit LVL says whether t is a row
@@ -401,54 +407,92 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     const IO *kg = reinterpret_cast<const IO *>(a.k);
     const IO *vg = reinterpret_cast<const IO *>(a.v);
 
-    // ---- phase 0: stage g, k, q with 16-byte loads, then into gate-thread registers ----
-    {
-        constexpr int KV = 16 / sizeof(IO);   // io elements per 16-byte load
-        for (int e = tid; e < C * (DK / KV); e += NTI) {
-            const int r = e / (DK / KV), c0 = (e % (DK / KV)) * KV;
-            f16x8 kv8, qv8;
-            if (r < L) {
-                const size_t off = ((size_t)(t0 + r) * a.hk + hk) * DK + c0;
-                if constexpr (KV == 8) {
-                    kv8 = load8_f16<IO>(kg + off);
-                    qv8 = load8_f16<IO>(qg + off);
-                } else {
-                    const f32x4 x = load4(kg + off), y = load4(qg + off);
+    // ---- phase 0: every input load issued at once; V stays in registers ----
+    constexpr int KV = 16 / sizeof(IO);                       // io elements per 16-byte load
+    constexpr int UKQ = C * DK / KV, UV = C * DV / KV, UG = C * DK / 4;
+    constexpr int NKQ = (UKQ + NTI - 1) / NTI, NV = (UV + NTI - 1) / NTI;
+    constexpr int NG = SCALAR ? 0 : (UG + NTI - 1) / NTI;
+    u32x4 kraw[NKQ], qraw[NKQ], vraw[NV];
+    f32x4 graw[NG > 0 ? NG : 1];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        kv8[u] = (_Float16)x[u];
-                        qv8[u] = (_Float16)y[u];
-                    }
-                }
-            } else {
-                kv8 = f16x8{};
-                qv8 = f16x8{};
-            }
+    for (int i = 0; i < NKQ; ++i) {
+        const int e = tid + i * NTI, r = e / (DK / KV), c0 = (e % (DK / KV)) * KV;
+        kraw[i] = qraw[i] = u32x4{0u, 0u, 0u, 0u};
+        if (e < UKQ && r < L) {
+            const size_t off = ((size_t)(t0 + r) * a.hk + hk) * DK + c0;
+            kraw[i] = *reinterpret_cast<const u32x4 *>(kg + off);
+            qraw[i] = *reinterpret_cast<const u32x4 *>(qg + off);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int e = tid + i * NTI, r = e / (DK / 4), c0 = (e % (DK / 4)) * 4;
+        graw[i] = zero4();
+        if (e < UG && r < L) graw[i] = *reinterpret_cast<const f32x4 *>(a.g + ((size_t)(t0 + r) * a.hv + h) * DK + c0);
+    }
+    float graw_s = 0.f, braw = 0.f;
+    if (tid < C && tid < L) {
+        if constexpr (SCALAR) graw_s = a.g[(size_t)(t0 + tid) * a.hv + h];
+        braw = a.beta[(size_t)(t0 + tid) * a.hv + h];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + i * NTI, r = e / (DV / KV), c0 = (e % (DV / KV)) * KV;
+        vraw[i] = u32x4{0u, 0u, 0u, 0u};
+        if (e < UV && r < L) vraw[i] = *reinterpret_cast<const u32x4 *>(vg + ((size_t)(t0 + r) * a.hv + h) * DV + c0);
+    }
+    // k, q as fp16 (exact for bf16 values in fp16 range), g as fp32, into LDS
+#pragma unroll
+    for (int i = 0; i < NKQ; ++i) {
+        const int e = tid + i * NTI, r = e / (DK / KV), c0 = (e % (DK / KV)) * KV;
+        if (e < UKQ) {
             if constexpr (KV == 8) {
-                *reinterpret_cast<f16x8 *>(&sm.u.in.k[r][c0]) = kv8;
-                *reinterpret_cast<f16x8 *>(&sm.u.in.q[r][c0]) = qv8;
+                f16x8 k8, q8;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    k8[2 * u] = (_Float16)__uint_as_float(kraw[i][u] << 16);
+                    k8[2 * u + 1] = (_Float16)__uint_as_float(kraw[i][u] & 0xffff0000u);
+                    q8[2 * u] = (_Float16)__uint_as_float(qraw[i][u] << 16);
+                    q8[2 * u + 1] = (_Float16)__uint_as_float(qraw[i][u] & 0xffff0000u);
+                }
+                *reinterpret_cast<f16x8 *>(&sm.u.in.k[r][c0]) = k8;
+                *reinterpret_cast<f16x8 *>(&sm.u.in.q[r][c0]) = q8;
             } else {
                 f16x4 k4, q4;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    k4[u] = kv8[u];
-                    q4[u] = qv8[u];
+                    k4[u] = (_Float16)__uint_as_float(kraw[i][u]);
+                    q4[u] = (_Float16)__uint_as_float(qraw[i][u]);
                 }
                 *reinterpret_cast<f16x4 *>(&sm.u.in.k[r][c0]) = k4;
                 *reinterpret_cast<f16x4 *>(&sm.u.in.q[r][c0]) = q4;
             }
         }
-        if constexpr (SCALAR) {
-            if (tid < C) sm.u.in.g[tid][0] = tid < L ? a.g[(size_t)(t0 + tid) * a.hv + h] : 0.f;
-        } else {
-            for (int e = tid; e < C * (DK / 4); e += NTI) {
-                const int r = e / (DK / 4), c0 = (e % (DK / 4)) * 4;
-                const f32x4 x = r < L ? *reinterpret_cast<const f32x4 *>(a.g + ((size_t)(t0 + r) * a.hv + h) * DK + c0)
-                                      : zero4();
-                *reinterpret_cast<f32x4 *>(&sm.u.in.g[r][c0]) = x;
-            }
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int e = tid + i * NTI, r = e / (DK / 4), c0 = (e % (DK / 4)) * 4;
+        if (e < UG) *reinterpret_cast<f32x4 *>(&sm.u.in.g[r][c0]) = graw[i];
+    }
+    if (tid < C) {
+        if constexpr (SCALAR) sm.u.in.g[tid][0] = graw_s;
+        sm.beta[tid] = braw;
+    }
+    __syncthreads();
+    // diagonal of M: q_r . k_r (gate factor 1), eight threads per token
+    {
+        constexpr int CPT = DK / 8;   // channels per thread
+        const int r = tid >> 3, part = tid & 7;
+        float d = 0.f;
+        if (r < C) {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c)
+                d += (float)sm.u.in.q[r][part * CPT + c] * (float)sm.u.in.k[r][part * CPT + c];
         }
-        if (tid < C) sm.beta[tid] = tid < L ? a.beta[(size_t)(t0 + tid) * a.hv + h] : 0.f;
+        d += __shfl_xor(d, 1, 64);
+        d += __shfl_xor(d, 2, 64);
+        d += __shfl_xor(d, 4, 64);
+        if (r < C && part == 0) sm.mdiag[r] = d;
     }
     __syncthreads();
     const bool fthread = tid < 4 * DK;
@@ -501,23 +545,6 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         case 4: mfma_level<4>(sm, wave, lane); break;
         default: mfma_level<5>(sm, wave, lane); break;
         }
-        if (lvl == 0 && wave >= 4) {
-            // diagonal of M: q_r . k_r (gate factor 1), four lanes per token
-            const int r = 16 * (wave - 4) + (lane >> 2), part = lane & 3;
-            float d = 0.f;
-            if (r < L) {
-                const size_t base = ((size_t)(t0 + r) * a.hk + hk) * DK + part * (DK / 4);
-#pragma unroll
-                for (int e = 0; e < DK / 4; e += 4) {
-                    const f32x4 x = load4(qg + base + e), y = load4(kg + base + e);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) d += (float)(_Float16)x[u] * (float)(_Float16)y[u];
-                }
-            }
-            d += __shfl_xor(d, 1, 64);
-            d += __shfl_xor(d, 2, 64);
-            if (part == 0) sm.u.m.T[r][r] = d;
-        }
         __syncthreads();
     }
 
@@ -558,20 +585,6 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     }
     __syncthreads();
 
-    // ---- waves 4..7: 16-byte loads of the V tile, in flight during the stores and the inversion ----
-    constexpr int VKV = 16 / sizeof(IO);               // io elements per 16-byte load
-    constexpr int VPT = C * (DV / VKV) / (NTI / 2);    // loads per value thread
-    u32x4 vraw[VPT];
-    if (wave >= 4) {
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int e = (tid - NTI / 2) + i * (NTI / 2);
-            const int r = e / (DV / VKV), c0 = (e % (DV / VKV)) * VKV;
-            vraw[i] = r < L ? *reinterpret_cast<const u32x4 *>(vg + ((size_t)(t0 + r) * a.hv + h) * DV + c0)
-                            : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-
     // ---- A-operand tile stores: Q exp(G) and M (lower triangle incl. diagonal) ----
     for (int e = tid; e < (C / 16) * (DK / 32) * 64; e += NTI) {
         const int tile = e >> 6, l = e & 63;
@@ -584,7 +597,8 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         const int r = 16 * (tile >> 1) + (l & 15), i0 = 32 * (tile & 1) + 8 * (l >> 4);
         f16x8 v;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (_Float16)(i0 + u <= r ? sm.u.m.T[r][i0 + u] : 0.f);
+        for (int u = 0; u < 8; ++u)
+            v[u] = (_Float16)(i0 + u < r ? sm.u.m.T[r][i0 + u] : i0 + u == r ? sm.mdiag[r] : 0.f);
         *reinterpret_cast<f16x8 *>(w.M + sh * C * C + (size_t)e * 8) = v;
     }
     __syncthreads();
@@ -654,16 +668,15 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     }
 
     // ---- (beta V)^T into the (now free) A region ----
-    if (wave >= 4) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int e = (tid - NTI / 2) + i * (NTI / 2);
-            const int r = e / (DV / VKV), c0 = (e % (DV / VKV)) * VKV;
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + i * NTI, r = e / (DV / KV), c0 = (e % (DV / KV)) * KV;
+        if (e < UV) {
             const float b = sm.beta[r];
 #pragma unroll
-            for (int u = 0; u < VKV; ++u) {
+            for (int u = 0; u < KV; ++u) {
                 float x;
-                if constexpr (VKV == 8) x = __uint_as_float(u & 1 ? (vraw[i][u >> 1] & 0xffff0000u) : (vraw[i][u >> 1] << 16));
+                if constexpr (KV == 8) x = __uint_as_float(u & 1 ? (vraw[i][u >> 1] & 0xffff0000u) : (vraw[i][u >> 1] << 16));
                 else x = __uint_as_float(vraw[i][u]);
                 const int j = c0 + u;
                 sm.u.m.r3.Vt[j][vt_col(j, r)] = (_Float16)(b * x);
