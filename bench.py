@@ -30,7 +30,7 @@ MFMA_F16_PEAK_TFLOPS = 2516.6    # MI355X dense fp16/bf16 MFMA, TFLOP/s
 METRIC = "KDA prefill tokens/s + MFMA util; decode states/s + HBM GB/s vs peak"
 DECODE_KERNEL = "kda::decode_kernel<128, 128, kda::bf16, float, false, true>"
 DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_51_amd", "csrc", "kda_decode.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_config5_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b4096_traffic.json")
 
 
 def _sha(path):
@@ -74,30 +74,38 @@ def decode_work(B, hk, hv, dk, dv):
     return B * hv * per
 
 
-def cpu_baseline(pre, dec):
+def cpu_baseline(pre, dec, reps=5, nreq=1024):
     """The fp64 oracle on the host cores, on a bounded sample of the same
-    workload: the full prefill batch (all 16 sequences, all heads) and 512 of
-    the 4096 decode requests."""
-    import numpy as np
+    workload: the full prefill batch (all 16 sequences, all heads; median of
+    ``reps`` runs) and the first ``nreq`` of the 4096 decode requests (median of
+    3 runs)."""
+    import statistics
     from oracle import oracle as O
     O.build(force=False)
     threads = O.max_threads()
     slots = O.map_slot(pre.indices.numpy(), pre.pool.shape[0])
     h0 = pre.pool[slots]
-    t = time.perf_counter()
-    O.prefill(pre.q, pre.k, pre.v, pre.g, pre.beta, pre.cu_seqlens, h0=h0)
-    tp = time.perf_counter() - t
+    tps = []
+    for _ in range(reps):
+        t = time.perf_counter()
+        O.prefill(pre.q, pre.k, pre.v, pre.g, pre.beta, pre.cu_seqlens, h0=h0)
+        tps.append(time.perf_counter() - t)
+    tp = statistics.median(tps)
     T = int(pre.cu_seqlens[-1])
-    nreq = 512
     dslots = O.map_slot(dec.indices.numpy()[:nreq], dec.pool.shape[0])
-    t = time.perf_counter()
-    O.decode(dec.q[:nreq], dec.k[:nreq], dec.v[:nreq], dec.g[:nreq], dec.beta[:nreq], dec.pool[dslots])
-    td = time.perf_counter() - t
+    pool = dec.pool[dslots]
+    tds = []
+    for _ in range(3):
+        t = time.perf_counter()
+        O.decode(dec.q[:nreq], dec.k[:nreq], dec.v[:nreq], dec.g[:nreq], dec.beta[:nreq], pool)
+        tds.append(time.perf_counter() - t)
+    td = statistics.median(tds)
     hv = dec.v.shape[1]
     return {
         "value": T / tp, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "sample": "fp64 C oracle (OpenMP over sequence-head units): full prefill batch "
-                  "(%d tokens x 32 heads) in %.2f s; decode: %d of 4096 requests in %.3f s" % (T, tp, nreq, td),
+                  "(%d tokens x 32 heads), median of %d runs = %.2f s; decode: first %d of 4096 "
+                  "requests, median of 3 runs = %.3f s" % (T, reps, tp, nreq, td),
         "decode_states_per_s": nreq * hv / td,
     }
 
@@ -127,10 +135,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    pre = W.config4()
-    dec = W.config5()
-    P = {n: getattr(pre, n).to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens", "pool", "indices")}
-    D = {n: getattr(dec, n).to(dev) for n in ("q", "k", "v", "g", "beta", "pool", "indices")}
+    do_pre = args.part in ("both", "prefill")
+    do_dec = args.part in ("both", "decode")
+    pre = W.kimi_prefill_16seq() if do_pre else None
+    dec = W.decode_b4096() if do_dec else None
+    P = {n: getattr(pre, n).to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens", "pool", "indices")} if do_pre else {}
+    D = {n: getattr(dec, n).to(dev) for n in ("q", "k", "v", "g", "beta", "pool", "indices")} if do_dec else {}
     torch.cuda.synchronize()
 
     if args.copy_calibration_gib > 0:
@@ -140,9 +150,6 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    do_pre = args.part in ("both", "prefill")
-    do_dec = args.part in ("both", "decode")
 
     def step(evs=None):
         if evs is not None:
@@ -170,13 +177,13 @@ def main():
     wall = time.perf_counter() - t0
     pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    finite = bool(torch.isfinite(P["pool"]).all().item()) and bool(torch.isfinite(D["pool"]).all().item())
+    finite = all(bool(torch.isfinite(X["pool"]).all().item()) for X in (P, D) if X)
 
-    cu = pre.cu_seqlens.tolist()
-    T = cu[-1]
     hk, hv, dk, dv = 32, 32, 128, 128
+    cu = pre.cu_seqlens.tolist() if do_pre else [0]
+    T = cu[-1]
     pf, pb = prefill_work(cu, hk, hv, dk, dv)
-    B = dec.q.shape[0]
+    B = dec.q.shape[0] if do_dec else 0
     db = decode_work(B, hk, hv, dk, dv)
 
     prefill = {"ms": pre_ms, "tokens_per_s": T / (pre_ms * 1e-3) if do_pre else None,
@@ -219,7 +226,7 @@ def main():
                    "global_batch": len(cu) - 1, "seq_len": T, "parallelism": "single-gpu"},
         "prefill": prefill, "decode": decode, "roofline": roof, "finite": finite,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and do_pre and do_dec:
         out["cpu_baseline"] = cpu_baseline(pre, dec)
     print(json.dumps(out))
 

@@ -114,16 +114,16 @@ kda_status kda_chunk_prefill(const kda_prefill_desc *d, const void *q, const voi
     if (N == 0) return KDA_OK;
     if (T == 0 && !final_state) return KDA_OK;
 
-    // Grids: intra (chunk slots, hv); state 1-D over (value tiles x hv x N),
-    // padded to a multiple of 8.
-    int dev = 0, max_x = 0, max_y = 0;
+    // Grids, all 1-D and padded to a multiple of 8: intra over (chunk slot,
+    // head) items; state over (value tile, head, sequence).
+    int dev = 0, max_x = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess)
+        hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess)
         return KDA_ERR_HIP;
     const long slots = (T + 63L * N) / 64;
+    const long intra_wgs = (slots * d->hv + 7) / 8 * 8;
     const long state_wgs = ((long)d->hv * N + 7) / 8 * 8 * 4;
-    if (slots > max_x || (long)d->hv > max_y || state_wgs > max_x) return KDA_ERR_UNSUPPORTED;
+    if (intra_wgs > max_x || state_wgs > max_x) return KDA_ERR_UNSUPPORTED;
 
     kda::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
@@ -161,13 +161,14 @@ kda_status kda_recurrent_decode(const kda_decode_desc *d, const void *q, const v
     for (const R &r : ins)
         if (overlap(o, o_b, r.p, r.n)) return KDA_ERR_ALIAS;
 
-    // Grid (dv / tile, B, hv) must fit the device's per-axis limits.
-    int dev = 0, max_y = 0, max_z = 0;
+    // Grid (hv x dv / tile, B) must fit the device's per-axis limits.
+    int dev = 0, max_x = 0, max_y = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_z, hipDeviceAttributeMaxGridDimZ, dev) != hipSuccess)
+        hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess)
         return KDA_ERR_HIP;
-    if ((long)d->batch > max_y || (long)d->hv > max_z) return KDA_ERR_UNSUPPORTED;
+    const long xdim = (long)d->hv * (d->dv / kda::decode_tile(d->dv));
+    if ((long)d->batch > max_y || xdim > max_x) return KDA_ERR_UNSUPPORTED;
 
     kda::DecodeArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state_pool;

@@ -6,7 +6,9 @@
 // row by row (each stored row j is one value channel, so rows are independent
 // given k, q, g), and writes the rows back in place.  The grid keeps batch and
 // head on separate axes (sglang PR 37317 digest, 实现拆解 item 1: folding them
-// into one axis overflowed the 65535 limit at large decode batches).  A
+// into one axis overflowed the 65535 limit at large decode batches): x runs
+// over (head, value tile), head-major, and y over the batch, so resident
+// workgroups stream the contiguous [Hv, V, K] block of one pool row.  A
 // negative slot index selects the last pool row (PR 30169 digest, 实现拆解
 // item 3).
 //
@@ -28,9 +30,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int tid = threadIdx.x;
     const int cg = tid % LPR;
     const int r0 = tid / LPR;
+    constexpr int NT_MAX = 128 / BV;
+    const int nt = a.dv / BV;   // value tiles per head (1 when BV = dv)
     const int b = blockIdx.y;
-    const int h = blockIdx.z;
-    const int j0 = blockIdx.x * BV;
+    const int h = NT_MAX == 1 ? (int)blockIdx.x : (int)blockIdx.x / nt;
+    const int j0 = NT_MAX == 1 ? 0 : ((int)blockIdx.x % nt) * BV;
     const int hk_idx = h / (a.hv / a.hk);
 
     int slot = a.indices[b];
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 template <int DK, int BV, typename IO, typename ST, bool SCALAR>
 static hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
     // The state block is touched once per call: stream it past the caches.
-    dim3 grid(a.dv / BV, a.batch, a.hv);
+    dim3 grid(a.hv * (a.dv / BV), a.batch);
     decode_kernel<DK, BV, IO, ST, SCALAR, true><<<grid, 256, 0, stream>>>(a);
     return hipGetLastError();
 }

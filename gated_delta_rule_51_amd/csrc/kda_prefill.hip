@@ -191,9 +191,12 @@ __device__ __forceinline__ void st16(float *Z, int ldz, const f32x4 &v, int lane
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) Z[(4 * kq + jj) * ldz + m] = v[jj];
 }
-// LDS writes of this wave are complete and visible to its other lanes.
+// LDS writes of this wave are complete and visible to its other lanes.  Only
+// the LDS counter is waited on (gfx9 s_waitcnt fields: vmcnt [3:0] and
+// [15:14], expcnt [6:4], lgkmcnt [11:8]; the others are left at their
+// maxima), so outstanding global stores and loads stay in flight.
 __device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
 }
 
@@ -210,6 +213,7 @@ __device__ __forceinline__ void wave_sync() {
 // rows go to LDS in fp16 and two 16x16 MFMA tiles per t-half build A and M.
 // ---------------------------------------------------------------------------
 constexpr int NTI = 512;   // threads of the intra kernel
+constexpr int kXcd = 8;    // XCDs of the device; workgroup ids go round robin over them
 
 template <int DK, int DV> struct IntraMain {
     union {
@@ -264,6 +268,15 @@ template <int DK, int DV> __device__ __forceinline__ float (*eighth_totals(Intra
     return reinterpret_cast<float (*)[DK]>(&sm.u.m.KGt[0][0]);
 }
 
+// Empty volatile statements that differ per arm: they keep a branch on a
+// wave-uniform condition from being merged into per-lane selects of both arms
+// (or into one loop over a selected array, which would leave the arrays in
+// scratch memory).
+template <int ARM> __device__ __forceinline__ void keep_branch() {
+    if constexpr (ARM == 0) asm volatile("; arm 0");
+    else asm volatile("; arm 1");
+}
+
 // Advance the chains from level LVL-1 to LVL and write this level's operand
 // rows: P[tau] / S[tau] hold (channel 2cp, channel 2cp+1) products as float2.
 template <int LVL, int DK, int DV>
@@ -286,9 +299,11 @@ __device__ __forceinline__ void factor_level(f32x2 (&P)[8], f32x2 (&S)[8], const
         if ((e8 & 1) == 0) {
 #pragma unroll
             for (int tau = 0; tau < 8; ++tau) S[tau] *= tot;
+            keep_branch<0>();
         } else {
 #pragma unroll
             for (int tau = 0; tau < 8; ++tau) P[tau] *= tot;
+            keep_branch<1>();
         }
     } else if constexpr (LVL == 5) {
         // 32-token blocks = eighths 4j..4j+3: the partner 16-token block's total
@@ -303,9 +318,11 @@ __device__ __forceinline__ void factor_level(f32x2 (&P)[8], f32x2 (&S)[8], const
         if ((e8 & 2) == 0) {
 #pragma unroll
             for (int tau = 0; tau < 8; ++tau) S[tau] *= tot;
+            keep_branch<0>();
         } else {
 #pragma unroll
             for (int tau = 0; tau < 8; ++tau) P[tau] *= tot;
+            keep_branch<1>();
         }
     }
     // operand rows: two channels per 4-byte write.  The row/column role is
@@ -329,9 +346,11 @@ __device__ __forceinline__ void factor_level(f32x2 (&P)[8], f32x2 (&S)[8], const
         if (row_bit<LVL>(e8, 0)) {
 #pragma unroll
             for (int tau = 0; tau < 8; ++tau) emit(tau, true, P[tau]);
+            keep_branch<0>();
         } else {
 #pragma unroll
             for (int tau = 0; tau < 8; ++tau) emit(tau, false, S[tau]);
+            keep_branch<1>();
         }
     }
     if constexpr (LVL == 3)   // eighth total (P over the whole eighth), read at levels 4 and 5
@@ -393,14 +412,21 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     IntraSmem<DK, DV> &sm = *reinterpret_cast<IntraSmem<DK, DV> *>(smem_raw);
 
-    const int slot = blockIdx.x, h = blockIdx.y;
+    // 1-D grid over (chunk slot, head) items, head fastest, so that resident
+    // workgroups read neighbouring tokens of every head (contiguous rows).
+    // Each XCD (ids round-robin over kXcd) takes one contiguous range.
+    const int n_items = w.slots * a.hv, per = (n_items + kXcd - 1) / kXcd;
+    const int item = (int)(blockIdx.x % kXcd) * per + (int)(blockIdx.x / kXcd);
+    if (item >= n_items) return;
+    const int slot = item / a.hv, h = item % a.hv;
     const int2 cm = w.chunk_map[slot];
     if (cm.x < 0) return;
     const int n = cm.x, jc = cm.y;
     const int t0 = a.cu_seqlens[n] + C * jc;
     const int L = min(C, a.cu_seqlens[n + 1] - t0);
     const int hk = h / (a.hv / a.hk);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const size_t sh = (size_t)slot * a.hv + h;
 
     const IO *qg = reinterpret_cast<const IO *>(a.q);
@@ -412,6 +438,15 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     constexpr int UKQ = C * DK / KV, UV = C * DV / KV, UG = C * DK / 4;
     constexpr int NKQ = (UKQ + NTI - 1) / NTI, NV = (UV + NTI - 1) / NTI;
     constexpr int NG = SCALAR ? 0 : (UG + NTI - 1) / NTI;
+    // Chunk bases are uniform; per-lane byte offsets stay below 64 rows of one
+    // token stride (< 2^32 for any grid the launch accepts).
+    const char *kb = reinterpret_cast<const char *>(kg + ((size_t)t0 * a.hk + hk) * DK);
+    const char *qb = reinterpret_cast<const char *>(qg + ((size_t)t0 * a.hk + hk) * DK);
+    const char *gb = reinterpret_cast<const char *>(a.g + ((size_t)t0 * a.hv + h) * (SCALAR ? 1 : DK));
+    const char *vb = reinterpret_cast<const char *>(vg + ((size_t)t0 * a.hv + h) * DV);
+    const float *bb = a.beta + (size_t)t0 * a.hv + h;
+    const unsigned kq_row = (unsigned)a.hk * DK * sizeof(IO), v_row = (unsigned)a.hv * DV * sizeof(IO);
+    const unsigned g_row = (unsigned)a.hv * (SCALAR ? 1 : DK) * 4;
     u32x4 kraw[NKQ], qraw[NKQ], vraw[NV];
     f32x4 graw[NG > 0 ? NG : 1];
 #pragma unroll
@@ -419,27 +454,27 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         const int e = tid + i * NTI, r = e / (DK / KV), c0 = (e % (DK / KV)) * KV;
         kraw[i] = qraw[i] = u32x4{0u, 0u, 0u, 0u};
         if (e < UKQ && r < L) {
-            const size_t off = ((size_t)(t0 + r) * a.hk + hk) * DK + c0;
-            kraw[i] = *reinterpret_cast<const u32x4 *>(kg + off);
-            qraw[i] = *reinterpret_cast<const u32x4 *>(qg + off);
+            const unsigned off = (unsigned)r * kq_row + (unsigned)c0 * sizeof(IO);
+            kraw[i] = *reinterpret_cast<const u32x4 *>(kb + off);
+            qraw[i] = *reinterpret_cast<const u32x4 *>(qb + off);
         }
     }
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
         const int e = tid + i * NTI, r = e / (DK / 4), c0 = (e % (DK / 4)) * 4;
         graw[i] = zero4();
-        if (e < UG && r < L) graw[i] = *reinterpret_cast<const f32x4 *>(a.g + ((size_t)(t0 + r) * a.hv + h) * DK + c0);
+        if (e < UG && r < L) graw[i] = *reinterpret_cast<const f32x4 *>(gb + (unsigned)r * g_row + (unsigned)c0 * 4);
     }
     float graw_s = 0.f, braw = 0.f;
     if (tid < C && tid < L) {
-        if constexpr (SCALAR) graw_s = a.g[(size_t)(t0 + tid) * a.hv + h];
-        braw = a.beta[(size_t)(t0 + tid) * a.hv + h];
+        if constexpr (SCALAR) graw_s = *reinterpret_cast<const float *>(gb + (unsigned)tid * g_row);
+        braw = bb[(unsigned)tid * a.hv];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * NTI, r = e / (DV / KV), c0 = (e % (DV / KV)) * KV;
         vraw[i] = u32x4{0u, 0u, 0u, 0u};
-        if (e < UV && r < L) vraw[i] = *reinterpret_cast<const u32x4 *>(vg + ((size_t)(t0 + r) * a.hv + h) * DV + c0);
+        if (e < UV && r < L) vraw[i] = *reinterpret_cast<const u32x4 *>(vb + (unsigned)r * v_row + (unsigned)c0 * sizeof(IO));
     }
     // k, q as fp16 (exact for bf16 values in fp16 range), g as fp32, into LDS
 #pragma unroll
@@ -479,7 +514,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         sm.beta[tid] = braw;
     }
     __syncthreads();
-    // diagonal of M: q_r . k_r (gate factor 1), eight threads per token
+    // ---- diagonal of M (q_r . k_r, gate factor 1) and gate-thread registers ----
     {
         constexpr int CPT = DK / 8;   // channels per thread
         const int r = tid >> 3, part = tid & 7;
@@ -496,7 +531,8 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     }
     __syncthreads();
     const bool fthread = tid < 4 * DK;
-    const int cp = tid % (DK / 2), e8 = tid / (DK / 2);   // channel pair, eighth (if fthread)
+    // channel pair, eighth (if fthread); with K = 128 the eighth is the wave
+    const int cp = tid % (DK / 2), e8 = DK == 128 ? wave : tid / (DK / 2);
     f32x2 P[8], S[8], H0, H1;
     f16x2 kr[8], qr[8];   // k, q of channels (2cp, 2cp+1), rounded to fp16 (exact for bf16 in range)
     if (fthread) {
@@ -557,18 +593,22 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
             w.GL[sh * DK + 2 * cp + 1] = gl[1];
         }
         f16x8 kg0, kg1, kl0, kl1;   // channels 2cp and 2cp+1, tokens 8 e8 .. 8 e8 + 7
+        const f32x2 one = {1.f, 1.f};
+        const f32x2 hp = e8 >= 4 ? H0 : one, hs = e8 < 4 ? H1 : one;
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) {
             const int t = 8 * e8 + tau;
-            const f32x2 gam = e8 >= 4 ? P[tau] * H0 : P[tau];     // exp(G_t)
-            const f32x2 rest = e8 < 4 ? S[tau] * H1 : S[tau];     // exp(G_last - G_t)
-            const float b = sm.beta[t];
+            const f32x2 gam = P[tau] * hp;     // exp(G_t)
+            const f32x2 rest = S[tau] * hs;    // exp(G_last - G_t)
+            const f32x2 bg = gam * sm.beta[t];
+            // fp16 x fp32 products rounded once to fp16 (mixed-precision FMA)
             const float k0 = (float)kr[tau][0], k1 = (float)kr[tau][1];
-            kg0[tau] = (_Float16)(b * k0 * gam[0]);
-            kg1[tau] = (_Float16)(b * k1 * gam[1]);
-            kl0[tau] = (_Float16)(k0 * rest[0]);
-            kl1[tau] = (_Float16)(k1 * rest[1]);
-            const f16x2 qgam = {(_Float16)((float)qr[tau][0] * gam[0]), (_Float16)((float)qr[tau][1] * gam[1])};
+            kg0[tau] = (_Float16)__builtin_fmaf(k0, bg[0], 0.f);
+            kg1[tau] = (_Float16)__builtin_fmaf(k1, bg[1], 0.f);
+            kl0[tau] = (_Float16)__builtin_fmaf(k0, rest[0], 0.f);
+            kl1[tau] = (_Float16)__builtin_fmaf(k1, rest[1], 0.f);
+            const f16x2 qgam = {(_Float16)__builtin_fmaf((float)qr[tau][0], gam[0], 0.f),
+                                (_Float16)__builtin_fmaf((float)qr[tau][1], gam[1], 0.f)};
             *reinterpret_cast<f16x2 *>(&sm.u.m.r1.stage[t][2 * cp]) = qgam;
         }
         // (the eighth totals held in the KGt space were last read at level 5)
@@ -751,7 +791,6 @@ template <int DK, int BV, typename IO> struct StateSmem {
 // go to different XCDs (round robin over kXcd); the value tiles of one
 // (sequence, head) are given ids kXcd apart so they share an XCD's L2 and the
 // second tile's operand reads hit it.  Rank-major: longest sequences first.
-constexpr int kXcd = 8;
 template <int NVT>
 __device__ __forceinline__ void state_unit(int id, int hv, int &vt, int &h, int &rank) {
     const int xcd = id % kXcd, slot = id / kXcd;
@@ -947,7 +986,8 @@ __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
 template <int DK, int DV, typename IO>
 hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
     const size_t smem = sizeof(IntraSmem<DK, DV>);
-    dim3 grid(w.slots, a.hv);
+    const long items = (long)w.slots * a.hv;
+    dim3 grid((unsigned)((items + kXcd - 1) / kXcd * kXcd));
     if (a.scalar_gate) {
         auto kern = intra_kernel<DK, DV, IO, true>;
         hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);

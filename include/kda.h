@@ -141,7 +141,8 @@ typedef struct {
  *   state_pool     [num_slots, hv, dv, dk] state dtype, read and written in place
  *   state_indices  [B] int32; an index < 0 selects slot num_slots - 1
  *   o     [B, hv, dv] io dtype
- * The launch grid is (dv / tile, B, hv): batch and head on separate axes.
+ * The launch grid is (hv x dv / tile, B): head (with value tile) on x and
+ * batch on y, so batch and head stay on separate axes.
  */
 kda_status kda_recurrent_decode(const kda_decode_desc *desc,
                                 const void *q, const void *k, const void *v,

@@ -136,27 +136,27 @@ def make_prefill(seed, lengths, hk, hv, dk, dv, io="bf16", gate="moderate",
     return inp
 
 
-def config1(seed=1):
+def single_seq_t128(seed=1):
     """One sequence of 128 tokens (two chunks), Hk=Hv=1, K=V=32, fp32 io,
     moderate per-channel gates, zero initial state."""
     return make_prefill(seed, [128], 1, 1, 32, 32, io="f32")
 
 
-def config2(seed=2):
+def varlen_gqa5(seed=2):
     """Five sequences, lengths U{1..130}, Hk=4, Hv=8, K=V=128, bf16 io,
     moderate gates, random fp32 initial states."""
     return make_prefill(seed, (5, 1, 130), 4, 8, 128, 128, h0="random")
 
 
-def config3(seed=11, state_dtype="f32"):
-    """Config 2's shapes in pool mode: 64-slot pool, slots drawn without
+def varlen_pool64(seed=11, state_dtype="f32"):
+    """The shapes of varlen_gqa5 in pool mode: 64-slot pool, slots drawn without
     replacement from [0, 63), the last sequence's index set to -1 (sentinel
     slot 63)."""
     return make_prefill(seed, (5, 1, 130), 4, 8, 128, 128, pool_slots=64,
                         state_dtype=state_dtype, pad_one=True)
 
 
-def config4(seed=4):
+def kimi_prefill_16seq(seed=4):
     """Kimi-Linear-shaped prefill: 16 sequences, lengths U{512..4096},
     Hk=Hv=32, K=V=128, bf16 io, realistic gates, fp32 pool of 32 slots."""
     return make_prefill(seed, (16, 512, 4096), 32, 32, 128, 128, gate="realistic",
@@ -202,7 +202,7 @@ def make_decode(seed, batch, hk, hv, dk, dv, num_slots, io="bf16", gate="realist
                             state_dtype=state_dtype, num_slots=num_slots))
 
 
-def config5(seed=5, batch=4096, num_slots=4160):
+def decode_b4096(seed=5, batch=4096, num_slots=4160):
     """Recurrent decode: 4096 one-token requests, Hk=Hv=32, K=V=128, bf16 io,
     realistic gates, fp32 pool of 4160 slots."""
     return make_decode(seed, batch, 32, 32, 128, 128, num_slots)

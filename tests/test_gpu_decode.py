@@ -99,7 +99,7 @@ def test_decode_full_size_sampled(K, oracle):
     pool of 4160 slots.  256 sampled requests are checked against the oracle
     and all untouched rows bitwise."""
     say("generating decode workload B=4096 Hv=32 pool 4160 slots")
-    d = W.config5()
+    d = W.decode_b4096()
     rng = np.random.default_rng(0)
     sample = np.sort(rng.choice(4096, 256, replace=False))
     check_decode(K, oracle, d, sample=sample)

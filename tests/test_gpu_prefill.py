@@ -39,27 +39,27 @@ def check(name, o, ht, o_ref, ht_ref, state_bf16=False):
     assert e_s <= (STATE_REL_BF16 if state_bf16 else STATE_REL_F32), name
 
 
-def test_config1_single_sequence_fp32(K, oracle):
-    inp = W.config1()
+def test_single_sequence_fp32(K, oracle):
+    inp = W.single_seq_t128()
     o, ht = run_dense(K, inp)
     o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
-    check("config1", o, ht, o_ref, ht_ref)
-    say("config1 o rel-L2 %.3e" % rel_l2(host(o), o_ref))
+    check("single_seq_t128", o, ht, o_ref, ht_ref)
+    say("single_seq_t128 o rel-L2 %.3e" % rel_l2(host(o), o_ref))
 
 
-def test_config2_varlen_gqa(K, oracle):
-    inp = W.config2()
+def test_varlen_gqa(K, oracle):
+    inp = W.varlen_gqa5()
     o, ht = run_dense(K, inp)
     o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=inp.h0)
-    check("config2", o, ht, o_ref, ht_ref)
+    check("varlen_gqa5", o, ht, o_ref, ht_ref)
 
 
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-def test_config3_pool_matches_dense_bitwise(K, oracle, state_dtype):
+def test_pool_matches_dense_bitwise(K, oracle, state_dtype):
     """Pool mode reproduces dense mode bit for bit: same o, the final states
     land in the indexed rows (the -1 index in the sentinel row), and every
     other row is untouched."""
-    inp = W.config3(state_dtype=state_dtype)
+    inp = W.varlen_pool64(state_dtype=state_dtype)
     S = inp.pool.shape[0]
     slots = oracle.map_slot(inp.indices.numpy(), S)
     pool_before = inp.pool.clone()
@@ -77,15 +77,15 @@ def test_config3_pool_matches_dense_bitwise(K, oracle, state_dtype):
     untouched[torch.as_tensor(slots)] = False
     assert torch.equal(pool.cpu()[untouched], pool_before[untouched])
     o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=h0_dense)
-    check("config3-%s" % state_dtype, o_p, pool[sl], o_ref, ht_ref, state_bf16=state_dtype == "bf16")
+    check("varlen_pool64-%s" % state_dtype, o_p, pool[sl], o_ref, ht_ref, state_bf16=state_dtype == "bf16")
 
 
-def test_config4_realistic_gates_full(K, oracle):
+def test_kimi_shaped_realistic_gates_full(K, oracle):
     """The bench workload: 16 sequences of 512..4096 tokens, Hk = Hv = 32,
     K = V = 128, realistic gates (in-chunk cumulative log-decay up to ~1e4),
     fp32 pool of 32 slots.  Every output and every written row is compared."""
     say("generating prefill workload (16 seqs, 512..4096 tokens, 32 heads)")
-    inp = W.config4()
+    inp = W.kimi_prefill_16seq()
     S = inp.pool.shape[0]
     slots = oracle.map_slot(inp.indices.numpy(), S)
     pool_before = inp.pool.clone()
@@ -95,7 +95,7 @@ def test_config4_realistic_gates_full(K, oracle):
     torch.cuda.synchronize()
     o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens,
                                    h0=pool_before[torch.as_tensor(slots)])
-    check("config4", o, pool[torch.as_tensor(slots).cuda()], o_ref, ht_ref)
+    check("kimi_prefill_16seq", o, pool[torch.as_tensor(slots).cuda()], o_ref, ht_ref)
     untouched = np.setdiff1d(np.arange(S), slots)
     assert torch.equal(pool[torch.as_tensor(untouched).cuda()].cpu(), pool_before[torch.as_tensor(untouched)])
 
