@@ -114,15 +114,15 @@ kda_status kda_chunk_prefill(const kda_prefill_desc *d, const void *q, const voi
     if (N == 0) return KDA_OK;
     if (T == 0 && !final_state) return KDA_OK;
 
-    // Grids, all 1-D and padded to a multiple of 8: intra over (chunk slot,
-    // head) items; state over (value tile, head, sequence).
+    // Grids, all 1-D: intra over (chunk slot, head) items, padded to a
+    // multiple of 8; state over (sequence, head) pairs.
     int dev = 0, max_x = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess)
         return KDA_ERR_HIP;
     const long slots = (T + 63L * N) / 64;
     const long intra_wgs = (slots * d->hv + 7) / 8 * 8;
-    const long state_wgs = ((long)d->hv * N + 7) / 8 * 8 * 4;
+    const long state_wgs = (long)d->hv * N;
     if (intra_wgs > max_x || state_wgs > max_x) return KDA_ERR_UNSUPPORTED;
 
     kda::PrefillArgs a{};

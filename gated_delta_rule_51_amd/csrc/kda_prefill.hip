@@ -41,7 +41,6 @@ namespace kda {
 namespace {
 
 constexpr int C = kChunk;   // 64
-constexpr int NT = 256;     // threads per workgroup
 constexpr int PADH = 8;     // fp16 row padding (16 B) against LDS bank conflicts
 constexpr int kOrderMax = 4096;   // sequences ranked by length in the meta kernel
 
@@ -772,7 +771,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 }
 
 // ---------------------------------------------------------------------------
-// state: per (value tile, sequence, value head), sequential over chunks
+// state: per (sequence, value head), sequential over chunks
 //
 // Operand layouts written by the intra kernel (fp16):
 //   A-operand tiles: tile (rt, kk) of an R x K matrix X holds, for lane l,
@@ -780,25 +779,27 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 //   accumulator tiles: tile (rt, ct) holds, for lane l,
 //     X[16 rt + 4 (l / 16) + jj][16 ct + l % 16], jj = 0..3  (8 B per lane)
 // so every operand load is one contiguous 16 B (or 8 B) access per lane.
+//
+// One workgroup of eight waves owns one (sequence, head) chain and the whole
+// K x V state.  Per chunk:
+//   (a) every wave writes its state tiles to LDS as fp16 (S^T, B operand);
+//   (b) waves 0..3 (token row tile rt = wave): U = Ut - W S  -> LDS (U^T);
+//       waves 4..7 (rt = wave - 4): the inter-chunk output part Q exp(G) S;
+//   (c) waves 4..7: O = scale (Q exp(G) S + M U), staged, stored as rows;
+//   (d) every wave: its state tiles S <- exp(G_last) S + (K exp(G_last - G))^T U.
+// Each operand register is reloaded with the next chunk's tile right after
+// its last use, so its load has a whole chunk step to arrive with a single
+// register copy; the register budget then admits two workgroups per CU and
+// every chain of a batch of up to 2 x CUs (sequence, head) pairs is resident
+// from the start.
 // ---------------------------------------------------------------------------
-template <int DK, int BV, typename IO> struct StateSmem {
-    _Float16 Sh[BV][DK + PADH];   // S^T as fp16 (B operand of W S and QG S)
-    _Float16 Vn[BV][C + PADH];    // U^T as fp16 (B operand of M U and KLt U)
-    IO Ost[4][16][BV + 16 / sizeof(IO)];   // per-wave output rows, for 16-byte stores
-};
+constexpr int NTS = 512;   // threads of the state kernel
 
-// Workgroup -> (value tile, head, sequence rank).  Consecutive workgroup ids
-// go to different XCDs (round robin over kXcd); the value tiles of one
-// (sequence, head) are given ids kXcd apart so they share an XCD's L2 and the
-// second tile's operand reads hit it.  Rank-major: longest sequences first.
-template <int NVT>
-__device__ __forceinline__ void state_unit(int id, int hv, int &vt, int &h, int &rank) {
-    const int xcd = id % kXcd, slot = id / kXcd;
-    vt = slot % NVT;
-    const int unit = (slot / NVT) * kXcd + xcd;     // (head, rank) pair index
-    h = unit % hv;
-    rank = unit / hv;
-}
+template <int DK, int DV, typename IO> struct StateSmem {
+    _Float16 Sh[DV][DK + PADH];   // S^T as fp16 (B operand of W S and Q exp(G) S)
+    _Float16 Vn[DV][C + PADH];    // U^T as fp16 (B operand of M U and KLt U)
+    IO Ost[4][16][DV + 16 / sizeof(IO)];   // output rows of waves 4..7, for 16-byte stores
+};
 
 template <typename ST> __device__ __forceinline__ f32x4 load_state4(const ST *p);
 template <> __device__ __forceinline__ f32x4 load_state4<float>(const float *p) {
@@ -816,29 +817,39 @@ __device__ __forceinline__ void store_state4(bf16 *p, const f32x4 &v) {
 __device__ __forceinline__ f16x8 gld8(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 __device__ __forceinline__ f16x4 gld4(const _Float16 *p) { return *reinterpret_cast<const f16x4 *>(p); }
 
-template <int DK, int DV, int BV, typename IO, typename ST>
-__global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
-    __shared__ __align__(16) StateSmem<DK, BV, IO> sm;
-    constexpr int KK = DK / 32;          // k-steps over key channels
-    constexpr int CT = BV / 16;          // value column tiles of this workgroup
-    constexpr int R = DK / 16;           // key row tiles of the state
-    constexpr int WPR = R >= 4 ? 1 : 4 / R;   // waves sharing one state row tile
-    constexpr int RPW = R >= 4 ? R / 4 : 1;   // state row tiles per wave
-    constexpr int CTW = CT / WPR;             // state column tiles per wave
-    static_assert(CTW >= 1, "tile");
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle; untyped 16-byte accesses with a byte range check.
+constexpr int kBufferWord3 = 0x00020000;
 
-    int vt, h, rank;
-    state_unit<DV / BV>(blockIdx.x, a.hv, vt, h, rank);
-    if (rank >= a.num_seqs) return;   // padding of the last XCD round
-    const int n = w.seq_order[rank];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// A wave-uniform element offset made opaque (both halves through
+// readfirstlane).  Added to a kernel-argument pointer it keeps the global
+// address space, and the compiler cannot fold per-lane offsets into a
+// loop-invariant 64-bit per-lane pointer per operand stream.
+__device__ __forceinline__ size_t uniform_off(size_t x) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+    return ((size_t)hi << 32) | lo;
+}
+
+// Per-wave part of one (sequence, head) chain; UW selects the role (U wave or
+// output wave).  Both roles pass the same barriers in the same order.
+template <bool UW, int DK, int DV, typename IO, typename ST>
+__device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w, StateSmem<DK, DV, IO> &sm,
+                                            int n, int h, int wave, int lane) {
+    constexpr int KK = DK / 32;               // k-steps over key channels
+    constexpr int CT = DV / 16;               // value column tiles
+    constexpr int R = DK / 16;                // key row tiles of the state
+    constexpr int NST = R * CT;               // state tiles
+    constexpr int NTW = NST >= 8 ? NST / 8 : 1;   // state tiles per wave (one key row tile)
+    static_assert(NTW <= CT, "a wave's state tiles share one key row tile");
     const int m = lane & 15, kq = lane >> 4;
-    const int j0 = vt * BV;
+    const int rt = wave & 3;                  // token row tile of (b) and (c)
+    const bool swave = NST >= 8 || wave * NTW < NST;   // holds state tiles
+    const int kr = (wave * NTW) / CT;         // its key row tile
+    const int ct0 = (wave * NTW) % CT;        // its first value column tile
     const int tbeg = a.cu_seqlens[n], tend = a.cu_seqlens[n + 1];
     const int nchunks = (tend - tbeg + C - 1) / C;
     const int s0 = w.chunk_off[n];
-    const int rt0 = (wave / WPR) * RPW;       // first state row tile of this wave
-    const int ct0 = (wave % WPR) * CTW;       // first state column tile of this wave
 
     long row_in = -1, row_out = -1;
     if (a.indices) {
@@ -849,135 +860,189 @@ __global__ __launch_bounds__(NT) void state_kernel(PrefillArgs a, Work w) {
         if (a.state_in) row_in = n;
         if (a.state_out) row_out = n;
     }
-    // S tiles: S[r][c] holds rows c = 16 (rt0 + r) + 4 kq + jj, cols j = 16 (ct0 + c) + m
-    f32x4 S[RPW][CTW];
-    const ST *sin = row_in >= 0 ? reinterpret_cast<const ST *>(a.state_in) + ((size_t)row_in * a.hv + h) * DV * DK
-                                : nullptr;
+    // S[c] holds state rows (key) 16 kr + 4 kq + jj, columns (value) 16 (ct0 + c) + m
+    f32x4 S[NTW];
+    {
+        const ST *sin = row_in >= 0 ? reinterpret_cast<const ST *>(a.state_in) + ((size_t)row_in * a.hv + h) * DV * DK
+                                    : nullptr;
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
+        for (int c = 0; c < NTW; ++c)
+            S[c] = (sin && swave) ? load_state4<ST>(sin + (size_t)(16 * (ct0 + c) + m) * DK + 16 * kr + 4 * kq)
+                                  : zero4();
+    }
+
+    // Operand registers of the current chunk (single copies, reloaded with
+    // the next chunk's tiles right after their last use).  Chunk bases are
+    // wave-uniform (see uniform_off); each lane adds a 32-bit byte offset.
+    f16x8 Xa[KK];                   // W (U waves) or Q exp(G) (output waves), row tile rt
+    f16x4 Ua[UW ? CT : 1];          // Ut of row tile rt (U waves)
+    f16x8 Ma[UW ? 1 : 2];           // M of row tile rt (output waves)
+    f16x8 Ka[2];                    // (K exp(G_last - G))^T, key row tile kr
+    f32x4 gl;                       // exp(G_last) of key rows 16 kr + 4 kq + jj
+    auto chunk_base = [&](int ch) { return (size_t)(s0 + ch) * a.hv + h; };
+    const unsigned lane16 = (unsigned)lane * 16u;
+    // The lane offset is re-derived behind an empty asm at every use, so the
+    // compiler cannot pre-add it to loop-invariant 64-bit per-lane pointers.
+    auto lane_off = [&](unsigned scale16) {
+        unsigned o = scale16 == 16u ? lane16 : lane16 >> 1;
+        asm volatile("" : "+v"(o));
+        return o;
+    };
+    auto ld8 = [](const _Float16 *base, unsigned off) {
+        return *reinterpret_cast<const f16x8 *>(reinterpret_cast<const char *>(base) + off);
+    };
+    auto ld4 = [](const _Float16 *base, unsigned off) {
+        return *reinterpret_cast<const f16x4 *>(reinterpret_cast<const char *>(base) + off);
+    };
+    auto load_x = [&](int ch) {
+        const size_t sh = chunk_base(ch);
+        const _Float16 *Xg = (UW ? w.W : w.QG) + uniform_off(sh * C * DK + (size_t)rt * KK * 512);
+        const unsigned lo16 = lane_off(16u);
 #pragma unroll
-        for (int c = 0; c < CTW; ++c)
-            S[r][c] = sin ? load_state4<ST>(sin + (size_t)(j0 + 16 * (ct0 + c) + m) * DK + 16 * (rt0 + r) + 4 * kq)
-                          : zero4();
+        for (int kk = 0; kk < KK; ++kk) Xa[kk] = ld8(Xg, lo16 + kk * 1024u);
+        if constexpr (UW) {
+            const _Float16 *Ug = w.Ut + uniform_off(sh * C * DV + (size_t)rt * CT * 256);
+            const unsigned lo8 = lane_off(8u);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) Ua[ct] = ld4(Ug, lo8 + ct * 512u);
+        }
+    };
+    auto load_m = [&](int ch) {
+        if constexpr (!UW) {
+            const _Float16 *Mg = w.M + uniform_off(chunk_base(ch) * C * C + (size_t)rt * 2 * 512);
+            const unsigned lo16 = lane_off(16u);
+            Ma[0] = ld8(Mg, lo16);
+            Ma[1] = ld8(Mg, lo16 + 1024u);
+        }
+    };
+    auto load_k = [&](int ch) {
+        const size_t sh = chunk_base(ch);
+        const _Float16 *Kg = w.KLt + uniform_off(sh * DK * C + (size_t)kr * 2 * 512);
+        const unsigned lo16 = lane_off(16u);
+        Ka[0] = ld8(Kg, lo16);
+        Ka[1] = ld8(Kg, lo16 + 1024u);
+        const float *Gg = w.GL + uniform_off(sh * DK + 16 * kr);
+        unsigned go = (unsigned)kq * 16u;
+        asm volatile("" : "+v"(go));
+        gl = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const char *>(Gg) + go);
+    };
+    if (nchunks > 0) {
+        load_x(0);
+        load_m(0);
+        if (swave) load_k(0);
+    }
 
     IO *og = reinterpret_cast<IO *>(a.o);
-    // Operands of one chunk for this wave (row tile `wave` of the chunk's
-    // tokens; the wave's state row tiles for KLt).  The next chunk's operands
-    // are loaded while the current chunk computes.
-    struct Ops {
-        f16x8 Wa[KK], Qa[KK], Ma[2], Ka[RPW][2];
-        f16x4 Ua[CT];
-        f32x4 gl[RPW];
-    };
-    auto load_ops = [&](int ch, Ops &op) {
-        const size_t sh = (size_t)(s0 + ch) * a.hv + h;
-        const _Float16 *Wg = w.W + sh * C * DK + (size_t)wave * KK * 512 + lane * 8;
-        const _Float16 *Qg = w.QG + sh * C * DK + (size_t)wave * KK * 512 + lane * 8;
-        const _Float16 *Mg = w.M + sh * C * C + (size_t)wave * 2 * 512 + lane * 8;
-        const _Float16 *Ug = w.Ut + sh * C * DV + ((size_t)wave * (DV / 16) + vt * CT) * 256 + lane * 4;
-        const _Float16 *Kg = w.KLt + sh * DK * C + lane * 8;
-        const float *GLg = w.GL + sh * DK;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            op.Wa[kk] = gld8(Wg + kk * 512);
-            op.Qa[kk] = gld8(Qg + kk * 512);
-        }
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) op.Ua[ct] = gld4(Ug + ct * 256);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) op.Ma[kk] = gld8(Mg + kk * 512);
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) op.Ka[r][kk] = gld8(Kg + ((size_t)(rt0 + r) * 2 + kk) * 512);
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) op.gl[r] = *reinterpret_cast<const f32x4 *>(GLg + 16 * (rt0 + r) + 4 * kq);
-    };
-    Ops cur, nxt;
-    if (nchunks > 0) load_ops(0, cur);
     for (int ch = 0; ch < nchunks; ++ch) {
         const int t0 = tbeg + ch * C;
         const int L = min(C, tend - t0);
-        if (ch + 1 < nchunks) load_ops(ch + 1, nxt);
-        const f16x8 *Wa = cur.Wa, *Qa = cur.Qa, *Ma = cur.Ma;
-        const f16x4 *Ua = cur.Ua;
-        const f32x4 *gl = cur.gl;
-        auto &Ka = cur.Ka;
+        // Operand reloads are unconditional (the last chunk reloads itself), so
+        // the number of memory operations between a load and its use is the
+        // same on every path and the waits stay exact.
+        const int nxt = min(ch + 1, nchunks - 1);
 
         // (a) S^T -> fp16 LDS
+        if (swave) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-            for (int c = 0; c < CTW; ++c) {
+            for (int c = 0; c < NTW; ++c) {
                 f16x4 hv4;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) hv4[jj] = (_Float16)S[r][c][jj];
-                *reinterpret_cast<f16x4 *>(&sm.Sh[16 * (ct0 + c) + m][16 * (rt0 + r) + 4 * kq]) = hv4;
+                for (int jj = 0; jj < 4; ++jj) hv4[jj] = (_Float16)S[c][jj];
+                *reinterpret_cast<f16x4 *>(&sm.Sh[16 * (ct0 + c) + m][16 * kr + 4 * kq]) = hv4;
             }
-        __syncthreads();
-        // (b) U = Ut - W S and the inter-chunk part of O, row tile `wave`
-        f32x4 Oacc[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            f32x4 ws = zero4(), qs = zero4();
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const f16x8 b = lds8(&sm.Sh[16 * ct + m][kk * 32 + kq * 8]);
-                ws = mfma_f16(Wa[kk], b, ws);
-                qs = mfma_f16(Qa[kk], b, qs);
-            }
-            Oacc[ct] = qs;
-            f16x4 uv;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) uv[jj] = (_Float16)((float)Ua[ct][jj] - ws[jj]);
-            *reinterpret_cast<f16x4 *>(&sm.Vn[16 * ct + m][16 * wave + 4 * kq]) = uv;
         }
         __syncthreads();
-        // (c) O += M U; write the valid rows
+
+        // (b) U = Ut - W S (U waves) | Q exp(G) S (output waves), row tile rt
+        [[maybe_unused]] f32x4 Oacc[UW ? 1 : CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                Oacc[ct] = mfma_f16(Ma[kk], lds8(&sm.Vn[16 * ct + m][kk * 32 + kq * 8]), Oacc[ct]);
+            for (int kk = 0; kk < KK; ++kk)
+                acc = mfma_f16(Xa[kk], lds8(&sm.Sh[16 * ct + m][kk * 32 + kq * 8]), acc);
+            if constexpr (UW) {
+                f16x4 uv;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                io_traits<IO>::store(&sm.Ost[wave][4 * kq + jj][0], 16 * ct + m, a.scale * Oacc[ct][jj]);
+                for (int jj = 0; jj < 4; ++jj) uv[jj] = (_Float16)((float)Ua[ct][jj] - acc[jj]);
+                *reinterpret_cast<f16x4 *>(&sm.Vn[16 * ct + m][16 * rt + 4 * kq]) = uv;
+            } else {
+                Oacc[ct] = acc;
+            }
+            // bound the hoisted LDS reads (register budget of the U waves)
+            if (UW || (ct & 1)) __builtin_amdgcn_sched_barrier(0);
         }
-        wave_sync();
-        {
-            // 16 rows x BV values of this wave -> 16-byte stores of the valid rows
-            constexpr int EPV = 16 / sizeof(IO), VPR = BV / EPV;   // elements per vector, vectors per row
+        load_x(nxt);
+        __syncthreads();
+
+        // (c) O = scale (Q exp(G) S + M U), output waves; valid rows stored
+        if constexpr (!UW) {
+            const int ow = wave - 4;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    Oacc[ct] = mfma_f16(Ma[kk], lds8(&sm.Vn[16 * ct + m][kk * 32 + kq * 8]), Oacc[ct]);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    io_traits<IO>::store(&sm.Ost[ow][4 * kq + jj][0], 16 * ct + m, a.scale * Oacc[ct][jj]);
+                if (ct & 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            load_m(nxt);
+            wave_sync();
+            // 16 rows x DV values of this wave -> 16-byte buffer stores.  The
+            // buffer's range is the valid rows of this tile, so the stores of
+            // rows past the sequence end are dropped by the hardware range
+            // check and no store is under a branch.
+            constexpr int EPV = 16 / sizeof(IO), VPR = DV / EPV;   // elements per vector, vectors per row
+            char *ob = reinterpret_cast<char *>(og + uniform_off(((size_t)(t0 + 16 * rt) * a.hv + h) * DV));
+            const int orow = a.hv * DV * (int)sizeof(IO);
+            const int nrec = __builtin_amdgcn_readfirstlane(max(0, min(16, L - 16 * rt)) * orow);   // bytes
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(ob, 0, nrec, kBufferWord3);
 #pragma unroll
             for (int e = lane; e < 16 * VPR; e += 64) {
                 const int rr = e / VPR, c0 = (e % VPR) * EPV;
-                const int r = 16 * wave + rr;
-                if (r < L)
-                    *reinterpret_cast<u32x4 *>(og + ((size_t)(t0 + r) * a.hv + h) * DV + j0 + c0) =
-                        *reinterpret_cast<const u32x4 *>(&sm.Ost[wave][rr][c0]);
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(&sm.Ost[ow][rr][c0]), orsrc,
+                                                       rr * orow + c0 * (int)sizeof(IO), 0, 0);
             }
         }
-        // (d) S = diag(exp G_last) S + KLt U
+
+        // (d) S = diag(exp G_last) S + KLt U, this wave's state tiles
+        if (swave) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r)
+            for (int c = 0; c < NTW; ++c) {
 #pragma unroll
-            for (int c = 0; c < CTW; ++c) {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) S[r][c][jj] *= gl[r][jj];
+                for (int jj = 0; jj < 4; ++jj) S[c][jj] *= gl[jj];
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    S[r][c] = mfma_f16(Ka[r][kk], lds8(&sm.Vn[16 * (ct0 + c) + m][kk * 32 + kq * 8]), S[r][c]);
+                    S[c] = mfma_f16(Ka[kk], lds8(&sm.Vn[16 * (ct0 + c) + m][kk * 32 + kq * 8]), S[c]);
+                if (c & 1) __builtin_amdgcn_sched_barrier(0);
             }
-        cur = nxt;
+            load_k(nxt);
+        }
     }
 
-    if (row_out >= 0) {
+    if (row_out >= 0 && swave) {
         ST *sout = reinterpret_cast<ST *>(a.state_out) + ((size_t)row_out * a.hv + h) * DV * DK;
 #pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-            for (int c = 0; c < CTW; ++c)
-                store_state4(sout + (size_t)(j0 + 16 * (ct0 + c) + m) * DK + 16 * (rt0 + r) + 4 * kq, S[r][c]);
+        for (int c = 0; c < NTW; ++c)
+            store_state4(sout + (size_t)(16 * (ct0 + c) + m) * DK + 16 * kr + 4 * kq, S[c]);
     }
+}
+
+template <int DK, int DV, typename IO, typename ST>
+__global__ __launch_bounds__(NTS, 4) void state_kernel(PrefillArgs a, Work w) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    StateSmem<DK, DV, IO> &sm = *reinterpret_cast<StateSmem<DK, DV, IO> *>(smem_raw);
+    // (sequence rank, head), rank-major: the longest sequences come first
+    const int unit = blockIdx.x;
+    const int h = unit % a.hv, rank = unit / a.hv;
+    if (rank >= a.num_seqs) return;
+    const int n = w.seq_order[rank];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave < 4) state_chain<true, DK, DV, IO, ST>(a, w, sm, n, h, wave, lane);    // U waves
+    else state_chain<false, DK, DV, IO, ST>(a, w, sm, n, h, wave, lane);   // output waves
 }
 
 // ---------------------------------------------------------------------------
@@ -1000,23 +1065,19 @@ hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int DK, int DV, int BV, typename IO>
-hipError_t launch_state_bv(PrefillArgs &a, Work &w, hipStream_t s) {
-    // 1-D grid over (value tile, head, sequence rank); see state_unit
-    const long units = (long)a.hv * a.num_seqs;
-    const long padded = (units + kXcd - 1) / kXcd * kXcd;
-    dim3 grid((unsigned)(padded * (DV / BV)));
-    if (a.state_bf16) state_kernel<DK, DV, BV, IO, bf16><<<grid, NT, 0, s>>>(a, w);
-    else state_kernel<DK, DV, BV, IO, float><<<grid, NT, 0, s>>>(a, w);
+template <int DK, int DV, typename IO, typename ST>
+hipError_t launch_state_st(PrefillArgs &a, Work &w, hipStream_t s) {
+    // 1-D grid over (sequence rank, head) pairs, rank-major
+    const size_t smem = sizeof(StateSmem<DK, DV, IO>);
+    auto kern = state_kernel<DK, DV, IO, ST>;
+    hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    kern<<<dim3((unsigned)((long)a.hv * a.num_seqs)), NTS, smem, s>>>(a, w);
     return hipGetLastError();
 }
 
 template <int DK, int DV, typename IO>
 hipError_t launch_state(PrefillArgs &a, Work &w, hipStream_t s) {
-    // 64-column value tiles (two per head at V = 128): measured fastest on
-    // MI355X for the 16 x 32-head workload (2.31 ms vs 2.37 ms whole-head).
-    constexpr int BV = DV < 64 ? DV : 64;
-    return launch_state_bv<DK, DV, BV, IO>(a, w, s);
+    return a.state_bf16 ? launch_state_st<DK, DV, IO, bf16>(a, w, s) : launch_state_st<DK, DV, IO, float>(a, w, s);
 }
 
 template <int DK, int DV, typename IO>
