@@ -35,10 +35,6 @@ struct PrefillArgs {
     int num_seqs, total_tokens, hk, hv, dk, dv, num_slots;
     float scale;
     bool io_bf16, state_bf16, scalar_gate;
-    // workspace carve-up (device pointers into the caller's buffer)
-    int chunk_slots;          // upper bound on the number of chunks
-    int32_t *chunk_map;       // [chunk_slots] (seq << 16 | local) or -1
-    void *ws_rest;            // chunk-level intermediates
 };
 
 size_t prefill_workspace_bytes(int num_seqs, int total_tokens, int hv, int dk, int dv);
