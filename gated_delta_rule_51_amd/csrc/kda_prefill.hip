@@ -724,7 +724,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     }
     __syncthreads();
 
-    // ---- W = T (beta K exp(G)) -> LDS stage;  Ut = T (beta V) -> global acc tiles ----
+    // ---- W = T (beta K exp(G)) -> LDS stage -> global tiles;  Ut = T (beta V) -> global acc tiles ----
     {
         const int m = lane & 15, kq = lane >> 4;
         const int rt = wave & 3, which = wave >> 2;
@@ -744,6 +744,14 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) sm.u.m.r1.stage[16 * rt + 4 * kq + jj][16 * ct + m] = (_Float16)acc[jj];
             }
+            // this wave's 16 staged rows -> its A-operand tiles (rt, kk) of W,
+            // with no workgroup barrier (the rows are this wave's own)
+            wave_sync();
+            _Float16 *Wg = w.W + sh * C * DK + (size_t)rt * (DK / 32) * 512;
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk)
+                *reinterpret_cast<f16x8 *>(Wg + ((size_t)kk * 64 + lane) * 8) =
+                    lds8(&sm.u.m.r1.stage[16 * rt + m][32 * kk + 8 * kq]);
         } else {
             _Float16 *Ug = w.Ut + sh * C * DV;
 #pragma unroll
@@ -756,16 +764,6 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
                 for (int jj = 0; jj < 4; ++jj) h4[jj] = (_Float16)acc[jj];
                 *reinterpret_cast<f16x4 *>(Ug + ((size_t)(rt * (DV / 16) + ct) * 64 + lane) * 4) = h4;
             }
-        }
-    }
-    __syncthreads();
-    {
-        _Float16 *Wg = w.W + sh * C * DK;
-        for (int e = tid; e < (C / 16) * (DK / 32) * 64; e += NTI) {
-            const int tile = e >> 6, l = e & 63;
-            const int rt = tile / (DK / 32), kk = tile % (DK / 32);
-            *reinterpret_cast<f16x8 *>(Wg + (size_t)e * 8) =
-                lds8(&sm.u.m.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]);
         }
     }
 }
