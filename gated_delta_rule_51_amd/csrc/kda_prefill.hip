@@ -633,6 +633,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     }
     for (int e = tid; e < (C / 16) * (C / 32) * 64; e += NTI) {
         const int tile = e >> 6, l = e & 63;
+        if ((tile & 1) && (tile >> 1) < 2) continue;   // rows < 32, columns >= 32: zero, never read
         const int r = 16 * (tile >> 1) + (l & 15), i0 = 32 * (tile & 1) + 8 * (l >> 4);
         f16x8 v;
 #pragma unroll
@@ -905,12 +906,15 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             for (int ct = 0; ct < CT; ++ct) Ua[ct] = ld4(Ug, lo8 + ct * 512u);
         }
     };
+    // M is lower triangular: the tile of token rows 16 rt.. and columns 32..63
+    // is zero (and not stored) for rt < 2.
+    const bool m_hi = rt >= 2;
     auto load_m = [&](int ch) {
         if constexpr (!UW) {
             const _Float16 *Mg = w.M + uniform_off(chunk_base(ch) * C * C + (size_t)rt * 2 * 512);
             const unsigned lo16 = lane_off(16u);
             Ma[0] = ld8(Mg, lo16);
-            Ma[1] = ld8(Mg, lo16 + 1024u);
+            Ma[1] = m_hi ? ld8(Mg, lo16 + 1024u) : f16x8{};
         }
     };
     auto load_k = [&](int ch) {
@@ -978,9 +982,8 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             const int ow = wave - 4;
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    Oacc[ct] = mfma_f16(Ma[kk], lds8(&sm.Vn[16 * ct + m][kk * 32 + kq * 8]), Oacc[ct]);
+                Oacc[ct] = mfma_f16(Ma[0], lds8(&sm.Vn[16 * ct + m][kq * 8]), Oacc[ct]);
+                if (m_hi) Oacc[ct] = mfma_f16(Ma[1], lds8(&sm.Vn[16 * ct + m][32 + kq * 8]), Oacc[ct]);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     io_traits<IO>::store(&sm.Ost[ow][4 * kq + jj][0], 16 * ct + m, a.scale * Oacc[ct][jj]);
