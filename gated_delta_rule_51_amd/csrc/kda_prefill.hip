@@ -648,42 +648,25 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         if ((i >> 4) > (r >> 4)) sm.u.m.T[r][i] = 0.f;
     }
 
-    // ---- T = (I + A)^-1 (blocked, fp32 MFMA, waves 0..3) ----
+    // ---- T = (I + A)^-1: diagonal blocks by forward substitution (wave 0) ----
+    // Each lane owns one column c of one 16x16 diagonal block b and runs the
+    // unit lower triangular forward substitution in fp32:
+    //   T_bb[r][c] = [r == c] - sum_{j < r} A_bb[r][j] T_bb[j][c]
+    // (rows above c come out exactly 0).
     constexpr int LD = C + 1;
-    if (wave < 4) {
-        float *scr = &sm.u.m.r1.scr[wave][0][0];
-        const int b = wave;
+    if (wave == 0) {
+        const int b = lane >> 4, c = lane & 15;
         const float *Ab = &sm.u.m.r3.A[16 * b][16 * b];
-        float *A2 = scr, *A4 = scr + 256, *X = scr + 512;
-        // (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) for strictly lower A
-        f32x4 v = mm16(Ab, LD, Ab, LD, lane);
-        st16(A2, 16, v, lane);
-        wave_sync();
-        v = mm16(A2, 16, A2, 16, lane);
-        st16(A4, 16, v, lane);
-        f32x4 a3 = mm16(Ab, LD, A2, 16, lane);
-        const int m = lane & 15, kq = lane >> 4;
-        f32x4 xv;
+        float t[16];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int r = 4 * kq + jj;
-            xv[jj] = (r == m ? 1.f : 0.f) - Ab[r * LD + m] + A2[r * 16 + m] - a3[jj];
+        for (int r = 0; r < 16; ++r) {
+            float acc = r == c ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc = __builtin_fmaf(-Ab[r * LD + j], t[j], acc);
+            t[r] = acc;
         }
-        wave_sync();
-        st16(X, 16, xv, lane);
-        wave_sync();
-        f32x4 t = mm16(X, 16, A4, 16, lane);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) xv[jj] += t[jj];
-        f32x4 a8 = mm16(A4, 16, A4, 16, lane);
-        wave_sync();
-        st16(A2, 16, a8, lane);
-        st16(X, 16, xv, lane);
-        wave_sync();
-        t = mm16(X, 16, A2, 16, lane);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) xv[jj] += t[jj];
-        st16(&sm.u.m.T[16 * b][16 * b], LD, xv, lane);
+        for (int r = 0; r < 16; ++r) sm.u.m.T[16 * b + r][16 * b + c] = t[r];
     }
     __syncthreads();
     // off-diagonal blocks by distance d: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
