@@ -221,7 +221,7 @@ template <int DK, int DV> struct IntraMain {
             _Float16 Fq[C / 2][DK + PADH];    // q * factor, row tokens (bit l removed)
         } f;
         _Float16 stage[C][DK + PADH];         // Q exp(G) staging, later W staging
-        float scr[4][3][256];                 // inversion scratch (16x16 fp32 blocks)
+        float scr[9][16][20];                 // inversion scratch (16x16 fp32 blocks)
     } r1;
     _Float16 KGt[DK][C + PADH];               // (beta K exp(G))^T
     union {
@@ -669,23 +669,50 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         for (int r = 0; r < 16; ++r) sm.u.m.T[16 * b + r][16 * b + c] = t[r];
     }
     __syncthreads();
-    // off-diagonal blocks by distance d: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
-    for (int d = 1; d <= 3; ++d) {
-        if (wave < 4 - d) {
-            float *X = &sm.u.m.r1.scr[wave][0][0];
-            const int b = wave, aa = b + d;
-            f32x4 acc = zero4();
-            for (int c = b; c < aa; ++c) {
-                const f32x4 t = mm16(&sm.u.m.r3.A[16 * aa][16 * c], LD, &sm.u.m.T[16 * c][16 * b], LD, lane);
+    // Off-diagonal blocks.  With D = I + (diagonal blocks of A), N = D^-1 A_off
+    // (N_ab = T_aa A_ab for a > b) is block strictly lower, so
+    // T = (I + N)^-1 D^-1 = (I - N + N^2 - N^3) D^-1, i.e. T_ab = Y_ab T_bb with
+    //   Y_10 = -N_10, Y_20 = -N_20 + N_21 N_10, Y_31 = -N_31 + N_32 N_21,
+    //   Y_30 = -N_30 + N_31 N_10 - N_32 Y_20,
+    // in three steps of independent 16x16 products (six, five, three waves).
+    {
+        constexpr int LS = 20;   // scratch leading dimension (bank spread of the fragment reads)
+        float(*scr)[16][LS] = sm.u.m.r1.scr;
+        float *Tm = &sm.u.m.T[0][0];
+        auto Tb = [&](int r, int c) { return Tm + (16 * r) * LD + 16 * c; };
+        auto Ab = [&](int r, int c) { return &sm.u.m.r3.A[16 * r][16 * c]; };
+        const int m = lane & 15, kq = lane >> 4;
+        // scratch blocks: 0..5 = N_10, N_21, N_32, N_20, N_31, N_30; 6 = Y_20, 7 = Y_31, 8 = Y_30
+        if (wave < 6) {
+            constexpr int pa[6] = {1, 2, 3, 2, 3, 3}, pb[6] = {0, 1, 2, 0, 1, 0};
+            const int ia = pa[wave], ib = pb[wave];
+            st16(&scr[wave][0][0], LS, mm16(Tb(ia, ia), LD, Ab(ia, ib), LD, lane), lane);
+        }
+        __syncthreads();
+        if (wave < 3) {   // T_{b+1,b} = -N_{b+1,b} T_bb
+            f32x4 t = mm16(&scr[wave][0][0], LS, Tb(wave, wave), LD, lane);
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[jj] += t[jj];
-            }
-            st16(X, 16, acc, lane);
+            for (int jj = 0; jj < 4; ++jj) t[jj] = -t[jj];
+            st16(Tb(wave + 1, wave), LD, t, lane);
+        } else if (wave < 5) {   // Y_20 (wave 3), Y_31 (wave 4)
+            const int i2 = wave == 3 ? 1 : 2, i1 = wave == 3 ? 0 : 1, in = wave == 3 ? 3 : 4;
+            f32x4 y = mm16(&scr[i2][0][0], LS, &scr[i1][0][0], LS, lane);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) y[jj] -= scr[in][4 * kq + jj][m];
+            st16(&scr[wave + 3][0][0], LS, y, lane);
+        }
+        __syncthreads();
+        if (wave < 2) {   // T_20 = Y_20 T_00, T_31 = Y_31 T_11
+            st16(Tb(wave + 2, wave), LD, mm16(&scr[6 + wave][0][0], LS, Tb(wave, wave), LD, lane), lane);
+        } else if (wave == 2) {   // Y_30, then T_30 = Y_30 T_00
+            const f32x4 t1 = mm16(&scr[4][0][0], LS, &scr[0][0][0], LS, lane);
+            const f32x4 t2 = mm16(&scr[2][0][0], LS, &scr[6][0][0], LS, lane);
+            f32x4 y;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) y[jj] = t1[jj] - t2[jj] - scr[5][4 * kq + jj][m];
+            st16(&scr[8][0][0], LS, y, lane);
             wave_sync();
-            f32x4 tv = mm16(&sm.u.m.T[16 * aa][16 * aa], LD, X, 16, lane);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) tv[jj] = -tv[jj];
-            st16(&sm.u.m.T[16 * aa][16 * b], LD, tv, lane);
+            st16(Tb(3, 0), LD, mm16(&scr[8][0][0], LS, Tb(0, 0), LD, lane), lane);
         }
         __syncthreads();
     }
