@@ -230,10 +230,9 @@ template <int DK, int DV> struct IntraMain {
     } r3;
     float T[C][C + 1];                        // M during the levels, then T = (I + A)^-1
 };
-// Input tiles, staged once with 16-byte loads; they alias IntraMain, which is
+// k and q tiles, staged once with 16-byte loads; they alias IntraMain, which is
 // not in use until the gate threads have copied them into registers.
 template <int DK> struct IntraInput {
-    float g[C][DK];
     _Float16 k[C][DK];
     _Float16 q[C][DK];
 };
@@ -434,9 +433,8 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 
     // ---- phase 0: every input load issued at once; V stays in registers ----
     constexpr int KV = 16 / sizeof(IO);                       // io elements per 16-byte load
-    constexpr int UKQ = C * DK / KV, UV = C * DV / KV, UG = C * DK / 4;
+    constexpr int UKQ = C * DK / KV, UV = C * DV / KV;
     constexpr int NKQ = (UKQ + NTI - 1) / NTI, NV = (UV + NTI - 1) / NTI;
-    constexpr int NG = SCALAR ? 0 : (UG + NTI - 1) / NTI;
     // Chunk bases are uniform; per-lane byte offsets stay below 64 rows of one
     // token stride (< 2^32 for any grid the launch accepts).
     const char *kb = reinterpret_cast<const char *>(kg + ((size_t)t0 * a.hk + hk) * DK);
@@ -447,7 +445,13 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     const unsigned kq_row = (unsigned)a.hk * DK * sizeof(IO), v_row = (unsigned)a.hv * DV * sizeof(IO);
     const unsigned g_row = (unsigned)a.hv * (SCALAR ? 1 : DK) * 4;
     u32x4 kraw[NKQ], qraw[NKQ], vraw[NV];
-    f32x4 graw[NG > 0 ? NG : 1];
+    // Gate threads: (channel pair cp: channels 2cp, 2cp+1; eighth e8: tokens
+    // 8 e8 .. 8 e8 + 7).  They load their g values straight into registers;
+    // one wave-wide load covers a whole 512-byte g row.  With K = 128 the
+    // eighth is the wave.
+    const bool fthread = tid < 4 * DK;
+    const int cp = tid % (DK / 2), e8 = DK == 128 ? wave : tid / (DK / 2);
+    f32x2 graw[8];
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) {
         const int e = tid + i * NTI, r = e / (DK / KV), c0 = (e % (DK / KV)) * KV;
@@ -459,16 +463,20 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         }
     }
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-        const int e = tid + i * NTI, r = e / (DK / 4), c0 = (e % (DK / 4)) * 4;
-        graw[i] = zero4();
-        if (e < UG && r < L) graw[i] = *reinterpret_cast<const f32x4 *>(gb + (unsigned)r * g_row + (unsigned)c0 * 4);
+    for (int tau = 0; tau < 8; ++tau) {
+        const int r = 8 * e8 + tau;
+        graw[tau] = f32x2{0.f, 0.f};
+        if (fthread && r < L) {
+            if constexpr (SCALAR) {
+                const float x = *reinterpret_cast<const float *>(gb + (unsigned)r * g_row);
+                graw[tau] = f32x2{x, x};
+            } else {
+                graw[tau] = *reinterpret_cast<const f32x2 *>(gb + (unsigned)r * g_row + (unsigned)cp * 8);
+            }
+        }
     }
-    float graw_s = 0.f, braw = 0.f;
-    if (tid < C && tid < L) {
-        if constexpr (SCALAR) graw_s = *reinterpret_cast<const float *>(gb + (unsigned)tid * g_row);
-        braw = bb[(unsigned)tid * a.hv];
-    }
+    float braw = 0.f;
+    if (tid < C && tid < L) braw = bb[(unsigned)tid * a.hv];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * NTI, r = e / (DV / KV), c0 = (e % (DV / KV)) * KV;
@@ -503,15 +511,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
             }
         }
     }
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-        const int e = tid + i * NTI, r = e / (DK / 4), c0 = (e % (DK / 4)) * 4;
-        if (e < UG) *reinterpret_cast<f32x4 *>(&sm.u.in.g[r][c0]) = graw[i];
-    }
-    if (tid < C) {
-        if constexpr (SCALAR) sm.u.in.g[tid][0] = graw_s;
-        sm.beta[tid] = braw;
-    }
+    if (tid < C) sm.beta[tid] = braw;
     __syncthreads();
     // ---- diagonal of M (q_r . k_r, gate factor 1) and gate-thread registers ----
     {
@@ -529,9 +529,6 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         if (r < C && part == 0) sm.mdiag[r] = d;
     }
     __syncthreads();
-    const bool fthread = tid < 4 * DK;
-    // channel pair, eighth (if fthread); with K = 128 the eighth is the wave
-    const int cp = tid % (DK / 2), e8 = DK == 128 ? wave : tid / (DK / 2);
     f32x2 P[8], S[8], H0, H1;
     f16x2 kr[8], qr[8];   // k, q of channels (2cp, 2cp+1), rounded to fp16 (exact for bf16 in range)
     if (fthread) {
@@ -539,11 +536,10 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         for (int tau = 0; tau < 8; ++tau) {
             const int r = 8 * e8 + tau;
             if constexpr (SCALAR) {
-                const float d = exp_f(sm.u.in.g[r][0]);
+                const float d = exp_f(graw[tau][0]);
                 P[tau] = f32x2{d, d};
             } else {
-                const f32x2 gv = *reinterpret_cast<const f32x2 *>(&sm.u.in.g[r][2 * cp]);
-                P[tau] = f32x2{exp_f(gv[0]), exp_f(gv[1])};
+                P[tau] = f32x2{exp_f(graw[tau][0]), exp_f(graw[tau][1])};
             }
             S[tau] = f32x2{1.f, 1.f};
             kr[tau] = *reinterpret_cast<const f16x2 *>(&sm.u.in.k[r][2 * cp]);
