@@ -33,6 +33,8 @@
 // Operands are fp16 (bf16 q/k/v inputs convert exactly; fp16's 11-bit
 // significand keeps the final-state error near 4e-4 relative, where bf16
 // operands would exceed 1e-3); accumulation is fp32; the state stays fp32.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -230,18 +232,11 @@ template <int DK, int DV> struct IntraMain {
     } r3;
     float T[C][C + 1];                        // M during the levels, then T = (I + A)^-1
 };
-// k and q tiles, staged once with 16-byte loads; they alias IntraMain, which is
-// not in use until the gate threads have copied them into registers.
-template <int DK> struct IntraInput {
-    _Float16 k[C][DK];
-    _Float16 q[C][DK];
-};
 template <int DK, int DV> struct IntraSmem {
     float beta[C];
     float mdiag[C];   // q_t . k_t, the diagonal of M
     union {
         IntraMain<DK, DV> m;
-        IntraInput<DK> in;
     } u;
 };
 
@@ -432,9 +427,12 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     const IO *vg = reinterpret_cast<const IO *>(a.v);
 
     // ---- phase 0: every input load issued at once; V stays in registers ----
+    // Gate threads (channel pair cp: channels 2cp, 2cp+1; eighth e8: tokens
+    // 8 e8 .. 8 e8 + 7) load their k, q and g values straight into registers:
+    // one wave-wide load covers a whole token row.  With K = 128 the eighth is
+    // the wave.  The V tile is loaded by all threads with 16-byte loads.
     constexpr int KV = 16 / sizeof(IO);                       // io elements per 16-byte load
-    constexpr int UKQ = C * DK / KV, UV = C * DV / KV;
-    constexpr int NKQ = (UKQ + NTI - 1) / NTI, NV = (UV + NTI - 1) / NTI;
+    constexpr int UV = C * DV / KV, NV = (UV + NTI - 1) / NTI;
     // Chunk bases are uniform; per-lane byte offsets stay below 64 rows of one
     // token stride (< 2^32 for any grid the launch accepts).
     const char *kb = reinterpret_cast<const char *>(kg + ((size_t)t0 * a.hk + hk) * DK);
@@ -444,29 +442,21 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     const float *bb = a.beta + (size_t)t0 * a.hv + h;
     const unsigned kq_row = (unsigned)a.hk * DK * sizeof(IO), v_row = (unsigned)a.hv * DV * sizeof(IO);
     const unsigned g_row = (unsigned)a.hv * (SCALAR ? 1 : DK) * 4;
-    u32x4 kraw[NKQ], qraw[NKQ], vraw[NV];
-    // Gate threads: (channel pair cp: channels 2cp, 2cp+1; eighth e8: tokens
-    // 8 e8 .. 8 e8 + 7).  They load their g values straight into registers;
-    // one wave-wide load covers a whole 512-byte g row.  With K = 128 the
-    // eighth is the wave.
     const bool fthread = tid < 4 * DK;
     const int cp = tid % (DK / 2), e8 = DK == 128 ? wave : tid / (DK / 2);
+    using Pair = typename std::conditional<sizeof(IO) == 2, unsigned, f32x2>::type;   // two io values
+    Pair kraw[8], qraw[8];
     f32x2 graw[8];
-#pragma unroll
-    for (int i = 0; i < NKQ; ++i) {
-        const int e = tid + i * NTI, r = e / (DK / KV), c0 = (e % (DK / KV)) * KV;
-        kraw[i] = qraw[i] = u32x4{0u, 0u, 0u, 0u};
-        if (e < UKQ && r < L) {
-            const unsigned off = (unsigned)r * kq_row + (unsigned)c0 * sizeof(IO);
-            kraw[i] = *reinterpret_cast<const u32x4 *>(kb + off);
-            qraw[i] = *reinterpret_cast<const u32x4 *>(qb + off);
-        }
-    }
+    u32x4 vraw[NV];
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
         const int r = 8 * e8 + tau;
+        kraw[tau] = qraw[tau] = Pair{};
         graw[tau] = f32x2{0.f, 0.f};
         if (fthread && r < L) {
+            const unsigned off = (unsigned)r * kq_row + (unsigned)cp * 2 * sizeof(IO);
+            kraw[tau] = *reinterpret_cast<const Pair *>(kb + off);
+            qraw[tau] = *reinterpret_cast<const Pair *>(qb + off);
             if constexpr (SCALAR) {
                 const float x = *reinterpret_cast<const float *>(gb + (unsigned)r * g_row);
                 graw[tau] = f32x2{x, x};
@@ -483,58 +473,27 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         vraw[i] = u32x4{0u, 0u, 0u, 0u};
         if (e < UV && r < L) vraw[i] = *reinterpret_cast<const u32x4 *>(vb + (unsigned)r * v_row + (unsigned)c0 * sizeof(IO));
     }
-    // k, q as fp16 (exact for bf16 values in fp16 range), g as fp32, into LDS
-#pragma unroll
-    for (int i = 0; i < NKQ; ++i) {
-        const int e = tid + i * NTI, r = e / (DK / KV), c0 = (e % (DK / KV)) * KV;
-        if (e < UKQ) {
-            if constexpr (KV == 8) {
-                f16x8 k8, q8;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    k8[2 * u] = (_Float16)__uint_as_float(kraw[i][u] << 16);
-                    k8[2 * u + 1] = (_Float16)__uint_as_float(kraw[i][u] & 0xffff0000u);
-                    q8[2 * u] = (_Float16)__uint_as_float(qraw[i][u] << 16);
-                    q8[2 * u + 1] = (_Float16)__uint_as_float(qraw[i][u] & 0xffff0000u);
-                }
-                *reinterpret_cast<f16x8 *>(&sm.u.in.k[r][c0]) = k8;
-                *reinterpret_cast<f16x8 *>(&sm.u.in.q[r][c0]) = q8;
-            } else {
-                f16x4 k4, q4;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    k4[u] = (_Float16)__uint_as_float(kraw[i][u]);
-                    q4[u] = (_Float16)__uint_as_float(qraw[i][u]);
-                }
-                *reinterpret_cast<f16x4 *>(&sm.u.in.k[r][c0]) = k4;
-                *reinterpret_cast<f16x4 *>(&sm.u.in.q[r][c0]) = q4;
-            }
-        }
+    // A: the diagonal blocks' diagonal and upper triangle are zero (while the loads are in flight)
+    for (int e = tid; e < 4 * 256; e += NTI) {
+        const int b = e >> 8, rr = (e >> 4) & 15, ii = e & 15;
+        if (ii >= rr) sm.u.m.r3.A[16 * b + rr][16 * b + ii] = 0.f;
     }
     if (tid < C) sm.beta[tid] = braw;
-    __syncthreads();
-    // ---- diagonal of M (q_r . k_r, gate factor 1) and gate-thread registers ----
-    {
-        constexpr int CPT = DK / 8;   // channels per thread
-        const int r = tid >> 3, part = tid & 7;
-        float d = 0.f;
-        if (r < C) {
-#pragma unroll
-            for (int c = 0; c < CPT; ++c)
-                d += (float)sm.u.in.q[r][part * CPT + c] * (float)sm.u.in.k[r][part * CPT + c];
-        }
-        d += __shfl_xor(d, 1, 64);
-        d += __shfl_xor(d, 2, 64);
-        d += __shfl_xor(d, 4, 64);
-        if (r < C && part == 0) sm.mdiag[r] = d;
-    }
-    __syncthreads();
+
+    // ---- gate-thread registers and the diagonal of M (q_t . k_t, gate factor 1) ----
     f32x2 P[8], S[8], H0, H1;
     f16x2 kr[8], qr[8];   // k, q of channels (2cp, 2cp+1), rounded to fp16 (exact for bf16 in range)
     if (fthread) {
+        float dpart[8];   // this thread's two-channel part of q_t . k_t
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) {
-            const int r = 8 * e8 + tau;
+            if constexpr (sizeof(IO) == 2) {
+                kr[tau] = f16x2{(_Float16)__uint_as_float(kraw[tau] << 16), (_Float16)__uint_as_float(kraw[tau] & 0xffff0000u)};
+                qr[tau] = f16x2{(_Float16)__uint_as_float(qraw[tau] << 16), (_Float16)__uint_as_float(qraw[tau] & 0xffff0000u)};
+            } else {
+                kr[tau] = f16x2{(_Float16)kraw[tau][0], (_Float16)kraw[tau][1]};
+                qr[tau] = f16x2{(_Float16)qraw[tau][0], (_Float16)qraw[tau][1]};
+            }
             if constexpr (SCALAR) {
                 const float d = exp_f(graw[tau][0]);
                 P[tau] = f32x2{d, d};
@@ -542,15 +501,30 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
                 P[tau] = f32x2{exp_f(graw[tau][0]), exp_f(graw[tau][1])};
             }
             S[tau] = f32x2{1.f, 1.f};
-            kr[tau] = *reinterpret_cast<const f16x2 *>(&sm.u.in.k[r][2 * cp]);
-            qr[tau] = *reinterpret_cast<const f16x2 *>(&sm.u.in.q[r][2 * cp]);
+            dpart[tau] = (float)qr[tau][0] * (float)kr[tau][0] + (float)qr[tau][1] * (float)kr[tau][1];
         }
-    }
-    __syncthreads();
-    // A: the diagonal blocks' diagonal and upper triangle are zero
-    for (int e = tid; e < 4 * 256; e += NTI) {
-        const int b = e >> 8, rr = (e >> 4) & 15, ii = e & 15;
-        if (ii >= rr) sm.u.m.r3.A[16 * b + rr][16 * b + ii] = 0.f;
+        // Sum over the DK / 2 lanes of this eighth by recursive halving: the
+        // first three exchange steps halve the eight partial sums, the rest
+        // are plain butterflies.  Afterwards the lane holds the total of token
+        // index 4 [bit G/2] + 2 [bit G/4] + [bit G/8] of its lane id.
+        constexpr int G = DK / 2;
+        auto halve = [&](int o, auto half) {   // keep one half of the values, add the partner's copy
+            constexpr int H = decltype(half)::value;
+            const bool up = (lane & o) != 0;
+#pragma unroll
+            for (int i = 0; i < H; ++i) {
+                const float send = up ? dpart[i] : dpart[i + H];
+                const float keep = up ? dpart[i + H] : dpart[i];
+                dpart[i] = keep + __shfl_xor(send, o, 64);
+            }
+        };
+        halve(G / 2, std::integral_constant<int, 4>{});
+        halve(G / 4, std::integral_constant<int, 2>{});
+        halve(G / 8, std::integral_constant<int, 1>{});
+#pragma unroll
+        for (int o = G / 16; o >= 1; o >>= 1) dpart[0] += __shfl_xor(dpart[0], o, 64);
+        const int idx = 4 * ((lane & (G / 2)) != 0) + 2 * ((lane & (G / 4)) != 0) + ((lane & (G / 8)) != 0);
+        if ((lane & (G / 8 - 1)) == 0) sm.mdiag[8 * e8 + idx] = dpart[0];
     }
     __syncthreads();
 
