@@ -21,6 +21,15 @@ q, k normalised in fp32 then cast, beta = sigmoid(N(0,1)), initial states
   inverse softplus of dt_c), which drives in-chunk cumulative log-decays to
   the 1e3..6e4 range.
 * scalar (GDN) gates: the same recipe with one value per (token, value head).
+
+Raw gate inputs for the fused-gate entry points (the GDN pool-mode test of
+sglang PR 30169's digest draws them this way: raw a, b in bf16, per-head
+A_log and dt_bias in fp32): ``gx`` = x and ``bx`` = the N(0,1) draw behind
+beta, both cast to the io dtype; ``A_log`` = a_c and ``dt_bias`` =
+dt_bias_c in fp32.  They come from the same draws as g and beta (no extra
+random numbers), but a kernel fed with them sees x and b rounded to the io
+dtype, so its expected values are computed from these raw tensors, not from
+g and beta.
 """
 from __future__ import annotations
 
@@ -60,12 +69,17 @@ def gate_params(gen, hv, dk, kind):
 
 
 def log_gates(gen, T, hv, dk, kind="moderate", scalar=False):
-    """g <= 0: [T, hv, dk] per channel, or [T, hv] for the scalar gate."""
+    """g <= 0: [T, hv, dk] per channel, or [T, hv] for the scalar gate, and the
+    raw draws it is made of: (g, x, a, dt_bias) with x [T, hv, dk] / [T, hv]
+    and a, dt_bias [hv, dk] / [hv]."""
     width = 1 if scalar else dk
     a, dt_bias = gate_params(gen, hv, width, kind)
     x = torch.randn(T, hv, width, generator=gen)
     g = -torch.exp(a)[None] * torch.nn.functional.softplus(x + dt_bias[None])
-    return g[..., 0].contiguous() if scalar else g.contiguous()
+    if scalar:
+        return g[..., 0].contiguous(), x[..., 0].contiguous(), a[:, 0].contiguous(), \
+            dt_bias[:, 0].contiguous()
+    return g.contiguous(), x.contiguous(), a.contiguous(), dt_bias.contiguous()
 
 
 def seq_lengths(gen, n, lo, hi):
@@ -92,6 +106,10 @@ class Prefill:
     indices: Optional[torch.Tensor] = None     # [N] int32, -1 = padding
     scale: float = 1.0
     meta: dict = field(default_factory=dict)
+    gx: Optional[torch.Tensor] = None          # raw gate input, io dtype, shape of g
+    A_log: Optional[torch.Tensor] = None       # [Hv, K] or [Hv] fp32
+    dt_bias: Optional[torch.Tensor] = None     # [Hv, K] or [Hv] fp32
+    bx: Optional[torch.Tensor] = None          # raw beta input [T, Hv], io dtype
 
     @property
     def num_seqs(self):
@@ -119,12 +137,14 @@ def make_prefill(seed, lengths, hk, hv, dk, dv, io="bf16", gate="moderate",
     q = unit_rows(gen, (T, hk, dk), dt)
     k = unit_rows(gen, (T, hk, dk), dt)
     v = torch.randn(T, hv, dv, generator=gen).to(dt)
-    beta = torch.sigmoid(torch.randn(T, hv, generator=gen))
-    g = log_gates(gen, T, hv, dk, gate, scalar_gate)
+    b = torch.randn(T, hv, generator=gen)
+    beta = torch.sigmoid(b)
+    g, x, a, dt_bias = log_gates(gen, T, hv, dk, gate, scalar_gate)
     sd = DTYPES[state_dtype]
     inp = Prefill(q, k, v, g, beta, cu, scale=scale,
                   meta=dict(seed=seed, hk=hk, hv=hv, dk=dk, dv=dv, io=io, gate=gate,
-                            scalar_gate=scalar_gate, state_dtype=state_dtype, T=T))
+                            scalar_gate=scalar_gate, state_dtype=state_dtype, T=T),
+                  gx=x.to(dt), A_log=a.float(), dt_bias=dt_bias.float(), bx=b.to(dt))
     if h0 == "random":
         inp.h0 = (torch.randn(n, hv, dv, dk, generator=gen) * 0.05).to(sd)
     if pool_slots:
@@ -174,6 +194,10 @@ class Decode:
     indices: torch.Tensor
     scale: float = 1.0
     meta: dict = field(default_factory=dict)
+    gx: Optional[torch.Tensor] = None          # raw gate input, io dtype, shape of g
+    A_log: Optional[torch.Tensor] = None       # [Hv, K] or [Hv] fp32
+    dt_bias: Optional[torch.Tensor] = None     # [Hv, K] or [Hv] fp32
+    bx: Optional[torch.Tensor] = None          # raw beta input [B, Hv], io dtype
 
 
 def make_decode(seed, batch, hk, hv, dk, dv, num_slots, io="bf16", gate="realistic",
@@ -187,8 +211,9 @@ def make_decode(seed, batch, hk, hv, dk, dv, num_slots, io="bf16", gate="realist
     q = unit_rows(gen, (batch, hk, dk), dt)
     k = unit_rows(gen, (batch, hk, dk), dt)
     v = torch.randn(batch, hv, dv, generator=gen).to(dt)
-    beta = torch.sigmoid(torch.randn(batch, hv, generator=gen))
-    g = log_gates(gen, batch, hv, dk, gate, scalar_gate)
+    braw = torch.randn(batch, hv, generator=gen)
+    beta = torch.sigmoid(braw)
+    g, x, a, dt_bias = log_gates(gen, batch, hv, dk, gate, scalar_gate)
     assert batch <= num_slots - 1
     idx = torch.randperm(num_slots - 1, generator=gen)[:batch].to(torch.int32)
     if pad:
@@ -199,7 +224,8 @@ def make_decode(seed, batch, hk, hv, dk, dv, num_slots, io="bf16", gate="realist
         pool[s] = torch.randn(hv, dv, dk, generator=gen) * 0.05
     return Decode(q, k, v, g, beta, pool, idx, scale,
                   meta=dict(seed=seed, batch=batch, hk=hk, hv=hv, dk=dk, dv=dv, io=io,
-                            state_dtype=state_dtype, num_slots=num_slots))
+                            state_dtype=state_dtype, num_slots=num_slots),
+                  gx=x.to(dt), A_log=a.float(), dt_bias=dt_bias.float(), bx=braw.to(dt))
 
 
 def decode_b4096(seed=5, batch=4096, num_slots=4160):

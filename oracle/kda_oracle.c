@@ -27,8 +27,10 @@
  * [T, Hv, K] (per channel) or [T, Hv] (scalar); beta is [T, Hv].  Value head h
  * reads key head h / (Hv / Hk).  Sequences are packed by cu_seqlens [N + 1].
  *
- * Inputs are float (bf16 and fp32 convert to float exactly); every operation
- * is done in double.  No blocking, no chunking, no reordering: one token at a
+ * q, k, v and the initial states are float (bf16 and fp32 convert to float
+ * exactly); g and beta are double, so that gates computed in fp64 from their
+ * raw inputs (oracle.gate_activation) enter unrounded.  Every operation is
+ * done in double.  No blocking, no chunking, no reordering: one token at a
  * time, in order.
  *
  * parity pinned by tests/test_oracle_pins.py (closed forms, invariants,
@@ -47,7 +49,7 @@ static void run_unit(int32_t t0, int32_t t1, int32_t h, int32_t hk_idx,
                      int32_t hk, int32_t hv, int32_t dk, int32_t dv,
                      int gate_scalar, double scale,
                      const float *q, const float *k, const float *v,
-                     const float *g, const float *beta,
+                     const double *g, const double *beta,
                      const float *h0_unit, /* [dv, dk] or NULL */
                      double *o, double *ht_unit, /* [dv, dk] or NULL */
                      double *S, double *pred, double *u)
@@ -61,12 +63,12 @@ static void run_unit(int32_t t0, int32_t t1, int32_t h, int32_t hk_idx,
         const float *qt = q + ((size_t)t * hk + hk_idx) * dk;
         const float *kt = k + ((size_t)t * hk + hk_idx) * dk;
         const float *vt = v + ((size_t)t * hv + h) * dv;
-        const double bt = (double)beta[(size_t)t * hv + h];
+        const double bt = beta[(size_t)t * hv + h];
 
         /* decay: row c of S scales by exp(g_t[c]) */
         for (int32_t c = 0; c < dk; ++c) {
-            const double gc = gate_scalar ? (double)g[(size_t)t * hv + h]
-                                          : (double)g[((size_t)t * hv + h) * dk + c];
+            const double gc = gate_scalar ? g[(size_t)t * hv + h]
+                                          : g[((size_t)t * hv + h) * dk + c];
             const double a = exp(gc);
             double *row = S + (size_t)c * dv;
             for (int32_t j = 0; j < dv; ++j) row[j] *= a;
@@ -115,7 +117,7 @@ int kdaref_prefill(int32_t num_seqs, const int32_t *cu_seqlens,
                    int32_t hk, int32_t hv, int32_t dk, int32_t dv,
                    int32_t gate_scalar, double scale,
                    const float *q, const float *k, const float *v,
-                   const float *g, const float *beta, const float *h0,
+                   const double *g, const double *beta, const float *h0,
                    double *o, double *ht, int32_t nthreads)
 {
     if (num_seqs < 0 || hk <= 0 || hv <= 0 || dk <= 0 || dv <= 0 || hv % hk != 0)

@@ -105,6 +105,13 @@ def _f32(x):
     return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
 
 
+def _f64(x):
+    """Exact conversion of a bf16/fp32/fp64 host array (numpy or torch) to float64."""
+    if hasattr(x, "detach"):  # torch tensor on the CPU
+        x = x.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data
 
@@ -117,7 +124,8 @@ def prefill(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0,
     beta: [T, Hv]; cu_seqlens: [N + 1]; h0: [N, Hv, V, K] or None (zeros).
     Returns (o [T, Hv, V] float64, ht [N, Hv, V, K] float64 or None).
     """
-    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    q, k, v = (_f32(x) for x in (q, k, v))
+    g, beta = _f64(g), _f64(beta)
     cu = np.ascontiguousarray(np.asarray(
         cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int32))
     n = cu.shape[0] - 1
@@ -138,6 +146,51 @@ def prefill(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0,
     if rc != 0:
         raise ValueError("kdaref_prefill rejected the shapes")
     return o, ht
+
+
+# ---------------------------------------------------------------------------
+# gate activation (fp64)
+# ---------------------------------------------------------------------------
+#
+# The log-decay gate and the write strength are produced from raw per-token
+# projections: g = -exp(A_log) * softplus(x + dt_bias) and beta = sigmoid(b)
+# (GDN pool-mode digest, sglang PR 30169, key-code test: per value head A_log
+# and dt_bias, raw a and b of shape [T, Hv]; KDA prefill digest, sglang
+# PR 27488, key-code extend wrapper: A_log and dt_bias handed to the kernel
+# entry).  For the per-channel (KDA) gate, x is [T, Hv, K] and A_log, dt_bias
+# are [Hv, K] (one pair per value head and key channel); for the scalar (GDN)
+# gate x is [T, Hv] and A_log, dt_bias are [Hv].
+
+def softplus(z):
+    """log(1 + e^z) in fp64, written as max(z, 0) + log1p(e^-|z|) so that
+    neither branch overflows."""
+    z = _f64(z)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def sigmoid(b):
+    """1 / (1 + e^-b) in fp64, evaluated through e^-|b| (no overflow)."""
+    b = _f64(b)
+    e = np.exp(-np.abs(b))
+    return np.where(b >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gate_activation(x, A_log, dt_bias):
+    """g = -exp(A_log) * softplus(x + dt_bias), fp64, broadcast over tokens.
+
+    x: [T, Hv, K] with A_log, dt_bias [Hv, K] (per channel), or x: [T, Hv]
+    with A_log, dt_bias [Hv] (scalar gate).  Returns g with the shape of x."""
+    x, A_log, dt_bias = _f64(x), _f64(A_log), _f64(dt_bias)
+    assert A_log.shape == x.shape[1:] and dt_bias.shape == x.shape[1:]
+    return -np.exp(A_log)[None] * softplus(x + dt_bias[None])
+
+
+def prefill_fused_gate(q, k, v, x, A_log, dt_bias, b, cu_seqlens, h0=None, scale=1.0,
+                       want_state=True, nthreads=0):
+    """Dense-mode prefill from raw gate inputs: the activation above, then the
+    recurrence (``prefill``) on the fp64 g and beta."""
+    return prefill(q, k, v, gate_activation(x, A_log, dt_bias), sigmoid(b), cu_seqlens,
+                   h0=h0, scale=scale, want_state=want_state, nthreads=nthreads)
 
 
 def map_slot(idx, num_slots):
@@ -179,7 +232,7 @@ def _gate_vec(g, t, h, dk):
 
 def recurrent_np(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0):
     """The recurrence again, in numpy: decay, residual, rank-1 write, read-out."""
-    q, k, v, g, beta = (np.asarray(_f32(x), dtype=np.float64) for x in (q, k, v, g, beta))
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     T, hk, dk = q.shape
     hv, dv = v.shape[1:]
@@ -203,7 +256,7 @@ def transition_np(q, k, v, g, beta, h0=None, scale=1.0):
     """Single sequence, brute force through explicit K x K transition matrices:
     S_t = (I - b_t k_t k_t^T) diag(exp g_t) S_{t-1} + b_t k_t v_t^T.
     Algebraically equal to the recurrence; shares none of its steps."""
-    q, k, v, g, beta = (np.asarray(_f32(x), dtype=np.float64) for x in (q, k, v, g, beta))
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     T, hk, dk = q.shape
     hv, dv = v.shape[1:]
     grp = hv // hk
@@ -243,7 +296,7 @@ def chunked_np(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0, chunk=64,
     for g <= 0).  Returns (o, ht) and, if asked, a list of per-chunk dicts
     (seq, head, t0, L, G, A, Tm, Ut, W, U, S0) in the GPU's storage orientation
     where that matters (S0 as [V, K])."""
-    q, k, v, g, beta = (np.asarray(_f32(x), dtype=np.float64) for x in (q, k, v, g, beta))
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     T, hk, dk = q.shape
     hv, dv = v.shape[1:]

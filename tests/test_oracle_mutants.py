@@ -16,8 +16,8 @@ ORACLE_C = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__
 
 DECAY = """        /* decay: row c of S scales by exp(g_t[c]) */
         for (int32_t c = 0; c < dk; ++c) {
-            const double gc = gate_scalar ? (double)g[(size_t)t * hv + h]
-                                          : (double)g[((size_t)t * hv + h) * dk + c];
+            const double gc = gate_scalar ? g[(size_t)t * hv + h]
+                                          : g[((size_t)t * hv + h) * dk + c];
             const double a = exp(gc);
             double *row = S + (size_t)c * dv;
             for (int32_t j = 0; j < dv; ++j) row[j] *= a;
@@ -52,7 +52,7 @@ MUTANTS = {
     # the gate indexed by the value channel (decay along V instead of K)
     "decay_along_v": [("for (int32_t j = 0; j < dv; ++j) row[j] *= a;",
                        "for (int32_t j = 0; j < dv; ++j) row[j] *= exp(gate_scalar ? gc : "
-                       "(double)g[((size_t)t * hv + h) * dk + (j % dk)]);")],
+                       "g[((size_t)t * hv + h) * dk + (j % dk)]);")],
     # final state written in math orientation instead of [V, K]
     "state_transposed": [("ht_unit[(size_t)j * dk + c] = S[(size_t)c * dv + j];",
                           "ht_unit[(size_t)c * dv + j] = S[(size_t)c * dv + j];")],
