@@ -9,7 +9,9 @@ One step = one pass of the whole path over one batch of synthetic input:
   * one-token recurrent decode of 4096 requests, Hk = Hv = 32, K = V = 128,
     bf16 q/k/v, fp32 state pool of 4160 slots updated in place.
 Inputs are generated on the host (seeded), copied to HBM before timing, and
-stay resident.  Prints one JSON line.
+stay resident.  After the timed steps the same workloads are passed through
+the fused-gate entry points (raw bf16 gate and beta inputs, activation inside
+the kernels) and reported under "fused_gate".  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 """
@@ -28,7 +30,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2516.6    # MI355X dense fp16/bf16 MFMA, TFLOP/s
 
 METRIC = "KDA prefill tokens/s + MFMA util; decode states/s + HBM GB/s vs peak"
-DECODE_KERNEL = "kda::decode_kernel<128, 128, kda::bf16, float, false, true>"
+DECODE_KERNEL = "kda::decode_kernel<128, 128, kda::bf16, float, false, false, true>"
 DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_51_amd", "csrc", "kda_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b4096_traffic.json")
 
@@ -53,25 +55,29 @@ def measured_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
-def prefill_work(cu, hk, hv, dk, dv, chunk=64):
+def prefill_work(cu, hk, hv, dk, dv, chunk=64, gate_bytes=4):
     """Algorithmic flops and bytes of one prefill call.
 
     flops per (token, value head): 6 K V (W S0, K~^T U, (Q G) S0) + C (3K + 2V)
     (A, W, M and Ut, M U; triangles counted half).  Bytes: q, k (shared by the
-    Hv/Hk value heads of a key head), v, g (fp32 per channel), beta, o per
-    token-head, plus h0 read and ht written per (sequence, head) in fp32."""
+    Hv/Hk value heads of a key head), v, g (per channel), beta, o per
+    token-head, plus h0 read and ht written per (sequence, head) in fp32.
+    ``gate_bytes`` is the size of one g / beta element: 4 for fp32 g and beta,
+    2 for the raw bf16 inputs of the fused-gate entry point (which also reads
+    A_log and dt_bias, 8 bytes per (head, channel), once)."""
     T = int(cu[-1])
     N = len(cu) - 1
     flops = T * hv * (6 * dk * dv + chunk * (3 * dk + 2 * dv))
-    per_tok = 2 * dk * 2 * hk / hv + 2 * dv + 4 * dk + 4 + 2 * dv
-    nbytes = T * hv * per_tok + N * hv * 2 * 4 * dk * dv
+    per_tok = 2 * dk * 2 * hk / hv + 2 * dv + gate_bytes * (dk + 1) + 2 * dv
+    nbytes = T * hv * per_tok + N * hv * 2 * 4 * dk * dv + (8 * hv * dk if gate_bytes != 4 else 0)
     return flops, nbytes
 
 
-def decode_work(B, hk, hv, dk, dv):
-    """Bytes per (request, head): fp32 state read + write, q, k, v, g, beta, o."""
-    per = 2 * 4 * dk * dv + (2 * dk * 2 * hk / hv + 2 * dv + 4 * dk + 4 + 2 * dv)
-    return B * hv * per
+def decode_work(B, hk, hv, dk, dv, gate_bytes=4):
+    """Bytes per (request, head): fp32 state read + write, q, k, v, g, beta, o
+    (g and beta elements of ``gate_bytes`` each, as for prefill_work)."""
+    per = 2 * 4 * dk * dv + (2 * dk * 2 * hk / hv + 2 * dv + gate_bytes * (dk + 1) + 2 * dv)
+    return B * hv * per + (8 * hv * dk if gate_bytes != 4 else 0)
 
 
 def cpu_baseline(pre, dec, reps=5, nreq=1024):
@@ -116,6 +122,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-gate-steps", type=int, default=10,
+                    help="after the timed steps, time this many passes through the fused-gate "
+                         "entry points (0: skip)")
     ap.add_argument("--part", choices=["both", "prefill", "decode"], default="both",
                     help="time one part only (for profiling runs)")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
@@ -139,8 +148,9 @@ def main():
     do_dec = args.part in ("both", "decode")
     pre = W.kimi_prefill_16seq() if do_pre else None
     dec = W.decode_b4096() if do_dec else None
-    P = {n: getattr(pre, n).to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens", "pool", "indices")} if do_pre else {}
-    D = {n: getattr(dec, n).to(dev) for n in ("q", "k", "v", "g", "beta", "pool", "indices")} if do_dec else {}
+    names = ("q", "k", "v", "g", "beta", "gx", "A_log", "dt_bias", "bx", "pool", "indices")
+    P = {n: getattr(pre, n).to(dev) for n in names + ("cu_seqlens",)} if do_pre else {}
+    D = {n: getattr(dec, n).to(dev) for n in names} if do_dec else {}
     torch.cuda.synchronize()
 
     if args.copy_calibration_gib > 0:
@@ -164,6 +174,19 @@ def main():
         if evs is not None:
             evs[2].record()
 
+    def fused_step(evs):
+        """The same pass through the fused-gate entry points (raw bf16 gate and
+        beta inputs activated inside the kernels)."""
+        evs[0].record()
+        if do_pre:
+            kda.chunk_prefill_fused_gate(P["q"], P["k"], P["v"], P["gx"], P["A_log"], P["dt_bias"], P["bx"],
+                                         P["cu_seqlens"], initial_state=P["pool"], state_indices=P["indices"])
+        evs[1].record()
+        if do_dec:
+            kda.recurrent_decode_fused_gate(D["q"], D["k"], D["v"], D["gx"], D["A_log"], D["dt_bias"],
+                                            D["bx"], D["pool"], D["indices"])
+        evs[2].record()
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -177,6 +200,17 @@ def main():
     wall = time.perf_counter() - t0
     pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    # fused-gate variant, timed after the step loop (not part of the step)
+    fsteps = args.fused_gate_steps
+    fused_pre_ms = fused_dec_ms = None
+    if fsteps > 0:
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(fsteps + 1)]
+        for e in fev:   # the first pass is a warm-up
+            fused_step(e)
+        torch.cuda.synchronize()
+        fused_pre_ms = sum(e[0].elapsed_time(e[1]) for e in fev[1:]) / fsteps
+        fused_dec_ms = sum(e[1].elapsed_time(e[2]) for e in fev[1:]) / fsteps
     finite = all(bool(torch.isfinite(X["pool"]).all().item()) for X in (P, D) if X)
 
     hk, hv, dk, dv = 32, 32, 128, 128
@@ -198,6 +232,20 @@ def main():
               "alg_gbs": db / (dec_ms * 1e-3) / 1e9 if do_dec else None}
     if do_dec:
         decode["hbm_frac_alg"] = decode["alg_gbs"] / HBM_PEAK_GBS
+    fused = None
+    if fsteps > 0:
+        io_b = 2   # bf16 raw gate and beta inputs
+        _, fpb = prefill_work(cu, hk, hv, dk, dv, gate_bytes=io_b)
+        fdb = decode_work(B, hk, hv, dk, dv, gate_bytes=io_b)
+        fused = {"steps": fsteps}
+        if do_pre:
+            fused["prefill"] = {"ms": fused_pre_ms, "tokens_per_s": T / (fused_pre_ms * 1e-3),
+                                "alg_gbs": fpb / (fused_pre_ms * 1e-3) / 1e9,
+                                "alg_tflops": pf / (fused_pre_ms * 1e-3) / 1e12}
+        if do_dec:
+            fused["decode"] = {"ms": fused_dec_ms, "states_per_s": B * hv / (fused_dec_ms * 1e-3),
+                               "alg_gbs": fdb / (fused_dec_ms * 1e-3) / 1e9,
+                               "hbm_frac_alg": fdb / (fused_dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
     # dominant kernel: the decode kernel (one launch per step, timed by the
     # events that bracket it on the stream it runs on)
@@ -225,6 +273,7 @@ def main():
                                "+ recurrent decode: B=4096, Hk=Hv=32, K=V=128, fp32 pool 4160 slots" % T,
                    "global_batch": len(cu) - 1, "seq_len": T, "parallelism": "single-gpu"},
         "prefill": prefill, "decode": decode, "roofline": roof, "finite": finite,
+        "fused_gate": fused,
     }
     if not args.no_cpu_baseline and do_pre and do_dec:
         out["cpu_baseline"] = cpu_baseline(pre, dec)

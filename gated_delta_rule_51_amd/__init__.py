@@ -11,8 +11,15 @@ anything else.
                                    scale=1.0, output_final_state=True)
     o = recurrent_decode(q, k, v, g, beta, state_pool, state_indices, scale=1.0)
 
+    # gate activation fused into the kernels: g = -exp(A_log) softplus(x + dt_bias),
+    # beta = sigmoid(b), from raw x, b in the io dtype
+    o, final_state = chunk_prefill_fused_gate(q, k, v, x, A_log, dt_bias, b, cu_seqlens, ...)
+    o = recurrent_decode_fused_gate(q, k, v, x, A_log, dt_bias, b, state_pool, state_indices)
+
 Layouts (contiguous): q, k [T, Hk, K]; v [T, Hv, V]; g [T, Hv, K] (per-channel
-gate) or [T, Hv] (scalar gate); beta [T, Hv] fp32; states [.., Hv, V, K].
+gate) or [T, Hv] (scalar gate); beta [T, Hv] fp32; states [.., Hv, V, K];
+raw x shaped like g and b like beta, both in the io dtype; A_log, dt_bias
+[Hv, K] (per channel) or [Hv] (scalar) fp32.
 """
 from __future__ import annotations
 
@@ -21,7 +28,8 @@ import os
 
 import torch
 
-__all__ = ["chunk_prefill", "recurrent_decode", "workspace_size", "library_path", "KdaError"]
+__all__ = ["chunk_prefill", "recurrent_decode", "chunk_prefill_fused_gate",
+           "recurrent_decode_fused_gate", "workspace_size", "library_path", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -73,6 +81,10 @@ def lib():
         L.kda_chunk_prefill.argtypes = [ctypes.POINTER(PrefillDesc)] + [_P] * 11 + [ctypes.c_size_t, _P]
         L.kda_recurrent_decode.restype = ctypes.c_int
         L.kda_recurrent_decode.argtypes = [ctypes.POINTER(DecodeDesc)] + [_P] * 9
+        L.kda_chunk_prefill_fused_gate.restype = ctypes.c_int
+        L.kda_chunk_prefill_fused_gate.argtypes = [ctypes.POINTER(PrefillDesc)] + [_P] * 13 + [ctypes.c_size_t, _P]
+        L.kda_recurrent_decode_fused_gate.restype = ctypes.c_int
+        L.kda_recurrent_decode_fused_gate.argtypes = [ctypes.POINTER(DecodeDesc)] + [_P] * 11
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_version.restype = ctypes.c_int32
@@ -134,19 +146,26 @@ def _workspace(device, stream, nbytes):
     return ws
 
 
-def chunk_prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_indices=None,
-                  scale=1.0, output_final_state=True, state_dtype=None):
-    """Chunked prefill over packed sequences.  Returns (o, final_state).
+def _gate_args(q, g, beta, raw):
+    """Check the gate inputs: (g, beta) fp32, or raw (x, A_log, dt_bias, b)."""
+    if raw is None:
+        _need(g, "g", torch.float32)
+        _need(beta, "beta", torch.float32, 2)
+        return (g, beta)
+    x, A_log, dt_bias, b = raw
+    _need(x, "gate_x", q.dtype)
+    _need(b, "beta_x", q.dtype, 2)
+    _need(A_log, "A_log", torch.float32, x.dim() - 1)
+    _need(dt_bias, "dt_bias", torch.float32, x.dim() - 1)
+    if A_log.shape != x.shape[1:] or dt_bias.shape != x.shape[1:]:
+        raise ValueError("A_log and dt_bias must have shape %s" % (tuple(x.shape[1:]),))
+    return raw
 
-    Dense mode (state_indices is None): initial_state [N, Hv, V, K] or None
-    (zeros); final_state is a new [N, Hv, V, K] tensor (or None when
-    output_final_state is False).  Pool mode: initial_state is the pool
-    [slots, Hv, V, K], updated in place at state_indices (negative -> last
-    slot), and returned as final_state."""
+
+def _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale, output_final_state,
+             state_dtype, raw):
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype, 3)
-    _need(g, "g", torch.float32)
-    _need(beta, "beta", torch.float32, 2)
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
     _need(initial_state, "initial_state", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
@@ -156,7 +175,7 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_ind
     hv, dv = v.shape[1], v.shape[2]
     pool = state_indices is not None
     sd = initial_state.dtype if initial_state is not None else (state_dtype or torch.float32)
-    desc = prefill_desc(q, v, g, N, sd, scale, initial_state.shape[0] if pool else 0)
+    desc = prefill_desc(q, v, gate[0], N, sd, scale, initial_state.shape[0] if pool else 0)
     o = torch.empty(T, hv, dv, dtype=q.dtype, device=dev)
     if pool:
         if initial_state is None:
@@ -169,25 +188,60 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_ind
     stream = _stream(dev)
     need = workspace_size(desc)
     ws = _workspace(dev, stream, need)
-    _check(lib().kda_chunk_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                   _ptr(cu_seqlens), _ptr(initial_state), _ptr(state_indices), fptr,
-                                   _ptr(o), _ptr(ws), ws.numel(), stream))
+    fn = lib().kda_chunk_prefill_fused_gate if raw else lib().kda_chunk_prefill
+    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate),
+              _ptr(cu_seqlens), _ptr(initial_state), _ptr(state_indices), fptr,
+              _ptr(o), _ptr(ws), ws.numel(), stream))
     return o, final
 
 
-def recurrent_decode(q, k, v, g, beta, state_pool, state_indices, scale=1.0):
-    """One-token decode for B requests, in place on the state pool.  Returns o."""
+def chunk_prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_indices=None,
+                  scale=1.0, output_final_state=True, state_dtype=None):
+    """Chunked prefill over packed sequences.  Returns (o, final_state).
+
+    Dense mode (state_indices is None): initial_state [N, Hv, V, K] or None
+    (zeros); final_state is a new [N, Hv, V, K] tensor (or None when
+    output_final_state is False).  Pool mode: initial_state is the pool
+    [slots, Hv, V, K], updated in place at state_indices (negative -> last
+    slot), and returned as final_state."""
+    gate = _gate_args(q, g, beta, None)
+    return _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale,
+                    output_final_state, state_dtype, False)
+
+
+def chunk_prefill_fused_gate(q, k, v, gate_x, A_log, dt_bias, beta_x, cu_seqlens, *,
+                             initial_state=None, state_indices=None, scale=1.0,
+                             output_final_state=True, state_dtype=None):
+    """chunk_prefill with g = -exp(A_log) softplus(gate_x + dt_bias) and
+    beta = sigmoid(beta_x) computed inside the kernels."""
+    gate = _gate_args(q, None, None, (gate_x, A_log, dt_bias, beta_x))
+    return _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale,
+                    output_final_state, state_dtype, True)
+
+
+def _decode(q, k, v, gate, state_pool, state_indices, scale, raw):
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype, 3)
-    _need(g, "g", torch.float32)
-    _need(beta, "beta", torch.float32, 2)
     _need(state_pool, "state_pool", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
     B, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     desc = DecodeDesc(B, hk, hv, dk, dv, _io_dtype(q), _DT[state_pool.dtype],
-                      GATE_SCALAR if g.dim() == 2 else GATE_CHANNEL, float(scale), state_pool.shape[0])
+                      GATE_SCALAR if gate[0].dim() == 2 else GATE_CHANNEL, float(scale), state_pool.shape[0])
     o = torch.empty(B, hv, dv, dtype=q.dtype, device=q.device)
-    _check(lib().kda_recurrent_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                      _ptr(state_pool), _ptr(state_indices), _ptr(o), _stream(q.device)))
+    fn = lib().kda_recurrent_decode_fused_gate if raw else lib().kda_recurrent_decode
+    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate),
+              _ptr(state_pool), _ptr(state_indices), _ptr(o), _stream(q.device)))
     return o
+
+
+def recurrent_decode(q, k, v, g, beta, state_pool, state_indices, scale=1.0):
+    """One-token decode for B requests, in place on the state pool.  Returns o."""
+    return _decode(q, k, v, _gate_args(q, g, beta, None), state_pool, state_indices, scale, False)
+
+
+def recurrent_decode_fused_gate(q, k, v, gate_x, A_log, dt_bias, beta_x, state_pool, state_indices,
+                                scale=1.0):
+    """recurrent_decode with the gate activation computed inside the kernel."""
+    gate = _gate_args(q, None, None, (gate_x, A_log, dt_bias, beta_x))
+    return _decode(q, k, v, gate, state_pool, state_indices, scale, True)

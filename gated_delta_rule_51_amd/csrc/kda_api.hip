@@ -44,47 +44,32 @@ kda_status check_decode_desc(const kda_decode_desc *d) {
 
 kda_status hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
-}  // namespace
+// The gate inputs of one call: activated fp32 g and beta, or (raw) the raw
+// projections x, b in the io dtype plus fp32 A_log and dt_bias.
+struct GateIn {
+    const void *g, *beta;
+    const float *A_log, *dt_bias;
+    bool raw;
+};
 
-extern "C" {
-
-const char *kda_status_string(kda_status s) {
-    switch (s) {
-    case KDA_OK: return "ok";
-    case KDA_ERR_NULL: return "a required pointer or descriptor is NULL";
-    case KDA_ERR_SHAPE: return "inconsistent or non-positive sizes";
-    case KDA_ERR_UNSUPPORTED: return "unsupported head dim, dtype, gate kind or grid size";
-    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
-    case KDA_ERR_ALIAS: return "an output aliases an input";
-    case KDA_ERR_HIP: return "HIP launch or runtime error";
-    case KDA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    }
-    return "unknown status";
-}
-
-int32_t kda_version(void) { return 100; }
-
-size_t kda_chunk_prefill_workspace_size(const kda_prefill_desc *d) {
-    if (check_desc(d) != KDA_OK) return 0;
-    return kda::prefill_workspace_bytes(d->num_seqs, d->total_tokens, d->hv, d->dk, d->dv);
-}
-
-kda_status kda_chunk_prefill(const kda_prefill_desc *d, const void *q, const void *k, const void *v,
-                             const float *g, const float *beta, const int32_t *cu_seqlens,
-                             void *state, const int32_t *state_indices, void *final_state, void *o,
-                             void *workspace, size_t workspace_bytes, void *stream) {
+kda_status prefill_impl(const kda_prefill_desc *d, const void *q, const void *k, const void *v,
+                        const GateIn &gi, const int32_t *cu_seqlens, void *state,
+                        const int32_t *state_indices, void *final_state, void *o, void *workspace,
+                        size_t workspace_bytes, void *stream) {
     kda_status st = check_desc(d);
     if (st != KDA_OK) return st;
     const bool pool = state_indices != nullptr;
     const long T = d->total_tokens, N = d->num_seqs;
     if (!cu_seqlens) return KDA_ERR_NULL;
-    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !gi.g || !gi.beta || !o)) return KDA_ERR_NULL;
+    if (T > 0 && gi.raw && (!gi.A_log || !gi.dt_bias)) return KDA_ERR_NULL;
     if (pool) {
         if (!state) return KDA_ERR_NULL;
         if (d->num_slots <= 0) return KDA_ERR_SHAPE;
         if (final_state && final_state != state) return KDA_ERR_ALIAS;
     }
-    const void *ptrs[] = {q, k, v, g, beta, cu_seqlens, state, state_indices, final_state, o, workspace};
+    const void *ptrs[] = {q, k, v, gi.g, gi.beta, gi.A_log, gi.dt_bias, cu_seqlens, state, state_indices,
+                          final_state, o, workspace};
     for (const void *p : ptrs)
         if (p && !aligned(p)) return KDA_ERR_ALIGN;
     const size_t need = kda::prefill_workspace_bytes(d->num_seqs, d->total_tokens, d->hv, d->dk, d->dv);
@@ -92,14 +77,17 @@ kda_status kda_chunk_prefill(const kda_prefill_desc *d, const void *q, const voi
 
     // o must not alias any input; a dense final_state must not alias inputs
     // other than the initial state.
-    const size_t isz = io_size(d->io_dtype), ssz = io_size(d->state_dtype);
+    const size_t isz = io_size(d->io_dtype), ssz = io_size(d->state_dtype), gsz = gi.raw ? isz : 4;
+    const size_t gw = d->gate == KDA_GATE_SCALAR ? 1 : (size_t)d->dk;
     const size_t qk_b = (size_t)T * d->hk * d->dk * isz, v_b = (size_t)T * d->hv * d->dv * isz;
-    const size_t g_b = (size_t)T * d->hv * (d->gate == KDA_GATE_SCALAR ? 1 : d->dk) * 4;
-    const size_t be_b = (size_t)T * d->hv * 4, cu_b = (size_t)(N + 1) * 4;
+    const size_t g_b = (size_t)T * d->hv * gw * gsz;
+    const size_t be_b = (size_t)T * d->hv * gsz, cu_b = (size_t)(N + 1) * 4;
+    const size_t par_b = gi.raw ? (size_t)d->hv * gw * 4 : 0;
     const size_t rows = pool ? (size_t)d->num_slots : (size_t)N;
     const size_t s_b = rows * d->hv * d->dv * d->dk * ssz;
     const size_t o_b = (size_t)T * d->hv * d->dv * isz;
-    struct R { const void *p; size_t n; } ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {g, g_b}, {beta, be_b},
+    struct R { const void *p; size_t n; } ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {gi.g, g_b}, {gi.beta, be_b},
+                                                   {gi.A_log, par_b}, {gi.dt_bias, par_b},
                                                    {cu_seqlens, cu_b}, {state, s_b},
                                                    {state_indices, pool ? (size_t)N * 4 : 0},
                                                    {workspace, need}};
@@ -126,7 +114,12 @@ kda_status kda_chunk_prefill(const kda_prefill_desc *d, const void *q, const voi
     if (intra_wgs > max_x || state_wgs > max_x) return KDA_ERR_UNSUPPORTED;
 
     kda::PrefillArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
+    a.q = q; a.k = k; a.v = v; a.cu_seqlens = cu_seqlens;
+    if (gi.raw) {
+        a.gx = gi.g; a.bx = gi.beta; a.A_log = gi.A_log; a.dt_bias = gi.dt_bias;
+    } else {
+        a.g = static_cast<const float *>(gi.g); a.beta = static_cast<const float *>(gi.beta);
+    }
     a.state_in = state;
     a.state_out = pool ? state : final_state;
     a.indices = state_indices;
@@ -138,24 +131,28 @@ kda_status kda_chunk_prefill(const kda_prefill_desc *d, const void *q, const voi
     a.io_bf16 = d->io_dtype == KDA_BF16;
     a.state_bf16 = d->state_dtype == KDA_BF16;
     a.scalar_gate = d->gate == KDA_GATE_SCALAR;
+    a.raw_gate = gi.raw;
     return hip_status(kda::launch_prefill(a, workspace, static_cast<hipStream_t>(stream)));
 }
 
-kda_status kda_recurrent_decode(const kda_decode_desc *d, const void *q, const void *k, const void *v,
-                                const float *g, const float *beta, void *state_pool,
-                                const int32_t *state_indices, void *o, void *stream) {
+kda_status decode_impl(const kda_decode_desc *d, const void *q, const void *k, const void *v,
+                       const GateIn &gi, void *state_pool, const int32_t *state_indices, void *o,
+                       void *stream) {
     kda_status st = check_decode_desc(d);
     if (st != KDA_OK) return st;
     if (d->batch == 0) return KDA_OK;
-    if (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !o) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g, beta, state_pool, state_indices, o};
+    if (!q || !k || !v || !gi.g || !gi.beta || !state_pool || !state_indices || !o) return KDA_ERR_NULL;
+    if (gi.raw && (!gi.A_log || !gi.dt_bias)) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, gi.g, gi.beta, gi.A_log, gi.dt_bias, state_pool, state_indices, o};
     for (const void *p : ptrs)
-        if (!aligned(p)) return KDA_ERR_ALIGN;
-    const size_t isz = io_size(d->io_dtype), B = d->batch;
+        if (p && !aligned(p)) return KDA_ERR_ALIGN;
+    const size_t isz = io_size(d->io_dtype), B = d->batch, gsz = gi.raw ? isz : 4;
+    const size_t gw = d->gate == KDA_GATE_SCALAR ? 1 : (size_t)d->dk;
     const size_t o_b = B * d->hv * d->dv * isz;
+    const size_t par_b = gi.raw ? (size_t)d->hv * gw * 4 : 0;
     struct R { const void *p; size_t n; } ins[] = {
         {q, B * d->hk * d->dk * isz}, {k, B * d->hk * d->dk * isz}, {v, o_b},
-        {g, B * d->hv * (d->gate == KDA_GATE_SCALAR ? 1 : d->dk) * 4}, {beta, B * d->hv * 4},
+        {gi.g, B * d->hv * gw * gsz}, {gi.beta, B * d->hv * gsz}, {gi.A_log, par_b}, {gi.dt_bias, par_b},
         {state_pool, (size_t)d->num_slots * d->hv * d->dv * d->dk * io_size(d->state_dtype)},
         {state_indices, B * 4}};
     for (const R &r : ins)
@@ -171,14 +168,80 @@ kda_status kda_recurrent_decode(const kda_decode_desc *d, const void *q, const v
     if ((long)d->batch > max_y || xdim > max_x) return KDA_ERR_UNSUPPORTED;
 
     kda::DecodeArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state_pool;
+    a.q = q; a.k = k; a.v = v; a.state = state_pool;
+    if (gi.raw) {
+        a.gx = gi.g; a.bx = gi.beta; a.A_log = gi.A_log; a.dt_bias = gi.dt_bias;
+    } else {
+        a.g = static_cast<const float *>(gi.g); a.beta = static_cast<const float *>(gi.beta);
+    }
     a.indices = state_indices; a.o = o;
     a.batch = d->batch; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
     a.num_slots = d->num_slots; a.scale = d->scale;
     a.io_bf16 = d->io_dtype == KDA_BF16;
     a.state_bf16 = d->state_dtype == KDA_BF16;
     a.scalar_gate = d->gate == KDA_GATE_SCALAR;
+    a.raw_gate = gi.raw;
     return hip_status(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer or descriptor is NULL";
+    case KDA_ERR_SHAPE: return "inconsistent or non-positive sizes";
+    case KDA_ERR_UNSUPPORTED: return "unsupported head dim, dtype, gate kind or grid size";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_ALIAS: return "an output aliases an input";
+    case KDA_ERR_HIP: return "HIP launch or runtime error";
+    case KDA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+int32_t kda_version(void) { return 200; }
+
+size_t kda_chunk_prefill_workspace_size(const kda_prefill_desc *d) {
+    if (check_desc(d) != KDA_OK) return 0;
+    return kda::prefill_workspace_bytes(d->num_seqs, d->total_tokens, d->hv, d->dk, d->dv);
+}
+
+kda_status kda_chunk_prefill(const kda_prefill_desc *d, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const int32_t *cu_seqlens,
+                             void *state, const int32_t *state_indices, void *final_state, void *o,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    const GateIn gi{g, beta, nullptr, nullptr, false};
+    return prefill_impl(d, q, k, v, gi, cu_seqlens, state, state_indices, final_state, o, workspace,
+                        workspace_bytes, stream);
+}
+
+kda_status kda_chunk_prefill_fused_gate(const kda_prefill_desc *d, const void *q, const void *k,
+                                        const void *v, const void *gate_x, const float *A_log,
+                                        const float *dt_bias, const void *beta_x,
+                                        const int32_t *cu_seqlens, void *state,
+                                        const int32_t *state_indices, void *final_state, void *o,
+                                        void *workspace, size_t workspace_bytes, void *stream) {
+    const GateIn gi{gate_x, beta_x, A_log, dt_bias, true};
+    return prefill_impl(d, q, k, v, gi, cu_seqlens, state, state_indices, final_state, o, workspace,
+                        workspace_bytes, stream);
+}
+
+kda_status kda_recurrent_decode(const kda_decode_desc *d, const void *q, const void *k, const void *v,
+                                const float *g, const float *beta, void *state_pool,
+                                const int32_t *state_indices, void *o, void *stream) {
+    const GateIn gi{g, beta, nullptr, nullptr, false};
+    return decode_impl(d, q, k, v, gi, state_pool, state_indices, o, stream);
+}
+
+kda_status kda_recurrent_decode_fused_gate(const kda_decode_desc *d, const void *q, const void *k,
+                                           const void *v, const void *gate_x, const float *A_log,
+                                           const float *dt_bias, const void *beta_x, void *state_pool,
+                                           const int32_t *state_indices, void *o, void *stream) {
+    const GateIn gi{gate_x, beta_x, A_log, dt_bias, true};
+    return decode_impl(d, q, k, v, gi, state_pool, state_indices, o, stream);
 }
 
 }  // extern "C"

@@ -19,7 +19,7 @@
 
 namespace kda {
 
-template <int DK, int BV, typename IO, typename ST, bool SCALAR, bool NT>
+template <int DK, int BV, typename IO, typename ST, bool SCALAR, bool RAW, bool NT>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int VEC = (sizeof(ST) == 4) ? 4 : 8;  // state elements per 16 B
     constexpr int LPR = DK / VEC;                    // lanes per stored row
@@ -78,20 +78,42 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             qq[i + e] = y[e];
         }
     }
-    if constexpr (SCALAR) {
-        const float d = exp_f(a.g[(long)b * a.hv + h]);
+    float beta;
+    if constexpr (RAW) {
+        // raw gate x (io dtype) activated here: exp(g), g = -exp(A_log) softplus(x + dt_bias)
+        const IO *xp = reinterpret_cast<const IO *>(a.gx);
+        if constexpr (SCALAR) {
+            const float x = io_traits<IO>::load(xp, (long)b * a.hv + h);
+            const float d = gate_decay((x + a.dt_bias[h]) * kLog2e, exp_f(a.A_log[h]));
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) dec[i] = d;
-    } else {
-        const float *gp = a.g + ((long)b * a.hv + h) * DK + c0;
+            for (int i = 0; i < VEC; ++i) dec[i] = d;
+        } else {
 #pragma unroll
-        for (int i = 0; i < VEC; i += 4) {
-            f32x4 x = *reinterpret_cast<const f32x4 *>(gp + i);
+            for (int i = 0; i < VEC; i += 4) {
+                const f32x4 x = load4(xp + ((long)b * a.hv + h) * DK + c0 + i);
+                const f32x4 al = *reinterpret_cast<const f32x4 *>(a.A_log + (long)h * DK + c0 + i);
+                const f32x4 db = *reinterpret_cast<const f32x4 *>(a.dt_bias + (long)h * DK + c0 + i);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dec[i + e] = exp_f(x[e]);
+                for (int e = 0; e < 4; ++e) dec[i + e] = gate_decay((x[e] + db[e]) * kLog2e, exp_f(al[e]));
+            }
         }
+        beta = sigmoid_f(io_traits<IO>::load(reinterpret_cast<const IO *>(a.bx), (long)b * a.hv + h));
+    } else {
+        if constexpr (SCALAR) {
+            const float d = exp_f(a.g[(long)b * a.hv + h]);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) dec[i] = d;
+        } else {
+            const float *gp = a.g + ((long)b * a.hv + h) * DK + c0;
+#pragma unroll
+            for (int i = 0; i < VEC; i += 4) {
+                f32x4 x = *reinterpret_cast<const f32x4 *>(gp + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dec[i + e] = exp_f(x[e]);
+            }
+        }
+        beta = a.beta[(long)b * a.hv + h];
     }
-    const float beta = a.beta[(long)b * a.hv + h];
     const IO *vp = reinterpret_cast<const IO *>(a.v) + ((long)b * a.hv + h) * a.dv + j0;
     IO *op = reinterpret_cast<IO *>(a.o) + ((long)b * a.hv + h) * a.dv + j0;
 
@@ -144,7 +166,10 @@ template <int DK, int BV, typename IO, typename ST, bool SCALAR>
 static hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
     // The state block is touched once per call: stream it past the caches.
     dim3 grid(a.hv * (a.dv / BV), a.batch);
-    decode_kernel<DK, BV, IO, ST, SCALAR, true><<<grid, 256, 0, stream>>>(a);
+    if (a.raw_gate)
+        decode_kernel<DK, BV, IO, ST, SCALAR, true, true><<<grid, 256, 0, stream>>>(a);
+    else
+        decode_kernel<DK, BV, IO, ST, SCALAR, false, true><<<grid, 256, 0, stream>>>(a);
     return hipGetLastError();
 }
 

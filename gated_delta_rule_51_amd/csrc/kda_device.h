@@ -30,6 +30,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // exp(x) through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Gate activation from raw inputs: the decay factor exp(g) for
+// g = -A softplus(z), A = exp(A_log), given zl = z log2(e) (z = x + dt_bias):
+//     exp(g) = 2^(-A sp),  sp = softplus(z) log2(e) = max(zl, 0) + log2(1 + 2^-|zl|).
+// Three hardware transcendentals.  log2 of the rounded 1 + 2^-|zl| costs at
+// most ~1e-7 of sp in absolute terms (relative accuracy is lost only where sp
+// itself is tiny), i.e. |error of g| <= ~1e-7 A: far below the rounding of a
+// bf16 x (2^-9 relative).
+__device__ __forceinline__ float gate_decay(float zl, float A) {
+    const float sp = __builtin_fmaxf(zl, 0.f) +
+                     __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-__builtin_fabsf(zl)));
+    return __builtin_amdgcn_exp2f(-A * sp);
+}
+
+// beta = sigmoid(b) = 1 / (1 + e^-b); e^-b overflowing to +inf gives 0.
+__device__ __forceinline__ float sigmoid_f(float b) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-b * kLog2e));
+}
+
 // Element type traits for io / state tensors.
 template <typename T> struct io_traits;
 template <> struct io_traits<float> {

@@ -9,13 +9,15 @@ namespace kda {
 
 struct DecodeArgs {
     const void *q, *k, *v;
-    const float *g, *beta;
+    const float *g, *beta;             // activated gate and beta (fp32), or
+    const void *gx, *bx;               // raw gate and beta inputs (io dtype) with
+    const float *A_log, *dt_bias;      // per-(head, channel) activation parameters
     void *state;
     const int32_t *indices;
     void *o;
     int batch, hk, hv, dk, dv, num_slots;
     float scale;
-    bool io_bf16, state_bf16, scalar_gate;
+    bool io_bf16, state_bf16, scalar_gate, raw_gate;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
@@ -26,7 +28,9 @@ constexpr int kChunk = 64;
 
 struct PrefillArgs {
     const void *q, *k, *v;
-    const float *g, *beta;
+    const float *g, *beta;             // activated gate and beta (fp32), or
+    const void *gx, *bx;               // raw gate and beta inputs (io dtype) with
+    const float *A_log, *dt_bias;      // per-(head, channel) activation parameters
     const int32_t *cu_seqlens;
     const void *state_in;     // dense h0, pool, or NULL
     void *state_out;          // dense ht, pool, or NULL
@@ -34,7 +38,7 @@ struct PrefillArgs {
     void *o;
     int num_seqs, total_tokens, hk, hv, dk, dv, num_slots;
     float scale;
-    bool io_bf16, state_bf16, scalar_gate;
+    bool io_bf16, state_bf16, scalar_gate, raw_gate;
 };
 
 size_t prefill_workspace_bytes(int num_seqs, int total_tokens, int hv, int dk, int dv);

@@ -400,7 +400,7 @@ __device__ __forceinline__ void mfma_level(IntraSmem<DK, DV> &sm, int wave, int 
     }
 }
 
-template <int DK, int DV, typename IO, bool SCALAR>
+template <int DK, int DV, typename IO, bool SCALAR, bool RAW>
 __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     IntraSmem<DK, DV> &sm = *reinterpret_cast<IntraSmem<DK, DV> *>(smem_raw);
@@ -437,36 +437,54 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     // token stride (< 2^32 for any grid the launch accepts).
     const char *kb = reinterpret_cast<const char *>(kg + ((size_t)t0 * a.hk + hk) * DK);
     const char *qb = reinterpret_cast<const char *>(qg + ((size_t)t0 * a.hk + hk) * DK);
-    const char *gb = reinterpret_cast<const char *>(a.g + ((size_t)t0 * a.hv + h) * (SCALAR ? 1 : DK));
+    // The gate arrives either as fp32 log-decays g and fp32 beta, or (RAW) as
+    // the raw projections x, b in the io dtype, activated here per element.
+    using GE = typename std::conditional<RAW, IO, float>::type;   // stored gate / beta element
+    const char *gb = reinterpret_cast<const char *>(RAW ? a.gx : static_cast<const void *>(a.g)) +
+                     ((size_t)t0 * a.hv + h) * (SCALAR ? 1 : DK) * sizeof(GE);
     const char *vb = reinterpret_cast<const char *>(vg + ((size_t)t0 * a.hv + h) * DV);
-    const float *bb = a.beta + (size_t)t0 * a.hv + h;
+    const GE *bb = reinterpret_cast<const GE *>(RAW ? a.bx : static_cast<const void *>(a.beta)) +
+                   (size_t)t0 * a.hv + h;
     const unsigned kq_row = (unsigned)a.hk * DK * sizeof(IO), v_row = (unsigned)a.hv * DV * sizeof(IO);
-    const unsigned g_row = (unsigned)a.hv * (SCALAR ? 1 : DK) * 4;
+    const unsigned g_row = (unsigned)a.hv * (SCALAR ? 1 : DK) * sizeof(GE);
     const bool fthread = tid < 4 * DK;
     const int cp = tid % (DK / 2), e8 = DK == 128 ? wave : tid / (DK / 2);
     using Pair = typename std::conditional<sizeof(IO) == 2, unsigned, f32x2>::type;   // two io values
+    using GPair = typename std::conditional<sizeof(GE) == 2, unsigned, f32x2>::type;  // two gate values
+    using GRaw = typename std::conditional<SCALAR, GE, GPair>::type;
     Pair kraw[8], qraw[8];
-    f32x2 graw[8];
+    GRaw graw[8];
     u32x4 vraw[NV];
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
         const int r = 8 * e8 + tau;
         kraw[tau] = qraw[tau] = Pair{};
-        graw[tau] = f32x2{0.f, 0.f};
+        graw[tau] = GRaw{};
         if (fthread && r < L) {
             const unsigned off = (unsigned)r * kq_row + (unsigned)cp * 2 * sizeof(IO);
             kraw[tau] = *reinterpret_cast<const Pair *>(kb + off);
             qraw[tau] = *reinterpret_cast<const Pair *>(qb + off);
+            graw[tau] = *reinterpret_cast<const GRaw *>(gb + (unsigned)r * g_row +
+                                                        (SCALAR ? 0u : (unsigned)cp * 2 * sizeof(GE)));
+        }
+    }
+    GE braw{};
+    if (tid < C && tid < L) braw = bb[(unsigned)tid * a.hv];
+    // per-(head, channel) activation parameters: a2 = exp(A_log), dtb = dt_bias log2(e)
+    f32x2 a2 = {0.f, 0.f}, dtb = {0.f, 0.f};
+    if constexpr (RAW) {
+        if (fthread) {
             if constexpr (SCALAR) {
-                const float x = *reinterpret_cast<const float *>(gb + (unsigned)r * g_row);
-                graw[tau] = f32x2{x, x};
+                a2 = f32x2{exp_f(a.A_log[h]), 0.f};
+                dtb = f32x2{a.dt_bias[h] * kLog2e, 0.f};
             } else {
-                graw[tau] = *reinterpret_cast<const f32x2 *>(gb + (unsigned)r * g_row + (unsigned)cp * 8);
+                const f32x2 al = *reinterpret_cast<const f32x2 *>(a.A_log + (size_t)h * DK + 2 * cp);
+                const f32x2 db = *reinterpret_cast<const f32x2 *>(a.dt_bias + (size_t)h * DK + 2 * cp);
+                a2 = f32x2{exp_f(al[0]), exp_f(al[1])};
+                dtb = f32x2{db[0] * kLog2e, db[1] * kLog2e};
             }
         }
     }
-    float braw = 0.f;
-    if (tid < C && tid < L) braw = bb[(unsigned)tid * a.hv];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * NTI, r = e / (DV / KV), c0 = (e % (DV / KV)) * KV;
@@ -478,7 +496,10 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         const int b = e >> 8, rr = (e >> 4) & 15, ii = e & 15;
         if (ii >= rr) sm.u.m.r3.A[16 * b + rr][16 * b + ii] = 0.f;
     }
-    if (tid < C) sm.beta[tid] = braw;
+    if (tid < C) {
+        if constexpr (RAW) sm.beta[tid] = tid < L ? sigmoid_f(io_traits<IO>::load(&braw, 0)) : 0.f;
+        else sm.beta[tid] = braw;
+    }
 
     // ---- gate-thread registers and the diagonal of M (q_t . k_t, gate factor 1) ----
     f32x2 P[8], S[8], H0, H1;
@@ -494,11 +515,28 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
                 kr[tau] = f16x2{(_Float16)kraw[tau][0], (_Float16)kraw[tau][1]};
                 qr[tau] = f16x2{(_Float16)qraw[tau][0], (_Float16)qraw[tau][1]};
             }
+            f32x2 gx;   // the two gate values of this token as fp32
             if constexpr (SCALAR) {
-                const float d = exp_f(graw[tau][0]);
+                const float x = io_traits<GE>::load(&graw[tau], 0);
+                gx = f32x2{x, x};
+            } else if constexpr (sizeof(GE) == 2) {
+                gx = f32x2{__uint_as_float(graw[tau] << 16), __uint_as_float(graw[tau] & 0xffff0000u)};
+            } else {
+                gx = graw[tau];
+            }
+            // (RAW: tokens past the chunk's end must keep factor 1, as a zero g does)
+            if constexpr (RAW && SCALAR) {
+                const float d = 8 * e8 + tau < L ? gate_decay(__builtin_fmaf(gx[0], kLog2e, dtb[0]), a2[0]) : 1.f;
+                P[tau] = f32x2{d, d};
+            } else if constexpr (RAW) {
+                P[tau] = 8 * e8 + tau < L ? f32x2{gate_decay(__builtin_fmaf(gx[0], kLog2e, dtb[0]), a2[0]),
+                                                  gate_decay(__builtin_fmaf(gx[1], kLog2e, dtb[1]), a2[1])}
+                                          : f32x2{1.f, 1.f};
+            } else if constexpr (SCALAR) {
+                const float d = exp_f(gx[0]);
                 P[tau] = f32x2{d, d};
             } else {
-                P[tau] = f32x2{exp_f(graw[tau][0]), exp_f(graw[tau][1])};
+                P[tau] = f32x2{exp_f(gx[0]), exp_f(gx[1])};
             }
             S[tau] = f32x2{1.f, 1.f};
             dpart[tau] = (float)qr[tau][0] * (float)kr[tau][0] + (float)qr[tau][1] * (float)kr[tau][1];
@@ -1034,15 +1072,10 @@ hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
     const size_t smem = sizeof(IntraSmem<DK, DV>);
     const long items = (long)w.slots * a.hv;
     dim3 grid((unsigned)((items + kXcd - 1) / kXcd * kXcd));
-    if (a.scalar_gate) {
-        auto kern = intra_kernel<DK, DV, IO, true>;
-        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        kern<<<grid, NTI, smem, s>>>(a, w);
-    } else {
-        auto kern = intra_kernel<DK, DV, IO, false>;
-        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        kern<<<grid, NTI, smem, s>>>(a, w);
-    }
+    auto kern = a.raw_gate ? (a.scalar_gate ? intra_kernel<DK, DV, IO, true, true> : intra_kernel<DK, DV, IO, false, true>)
+                           : (a.scalar_gate ? intra_kernel<DK, DV, IO, true, false> : intra_kernel<DK, DV, IO, false, false>);
+    hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    kern<<<grid, NTI, smem, s>>>(a, w);
     return hipGetLastError();
 }
 

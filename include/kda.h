@@ -125,6 +125,36 @@ kda_status kda_chunk_prefill(const kda_prefill_desc *desc,
                              void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/*
+ * Chunked prefill with the gate activation fused in: instead of fp32 g and
+ * beta, the raw per-token projections are passed and activated inside the
+ * first kernel,
+ *     g    = -exp(A_log) * softplus(gate_x + dt_bias)
+ *     beta = sigmoid(beta_x)
+ * (GDN pool-mode digest, sglang PR 30169, key-code test: raw a and b in bf16
+ * per (token, value head), A_log and dt_bias per value head; KDA prefill
+ * digest, PR 27488, key-code extend wrapper: A_log and dt_bias handed to the
+ * kernel entry).
+ *   gate_x   [T, hv, dk] (CHANNEL) or [T, hv] (SCALAR), io dtype
+ *   A_log    [hv, dk] (CHANNEL) or [hv] (SCALAR), fp32; a per-head A_log is
+ *            passed broadcast over the channels for the CHANNEL gate
+ *   dt_bias  same shape as A_log, fp32
+ *   beta_x   [T, hv] io dtype
+ * Everything else (shapes, pool mode, aliasing, workspace, errors) is as for
+ * kda_chunk_prefill, with gate_x, A_log, dt_bias and beta_x in the roles of
+ * g and beta.  The activation runs in fp32: softplus through max(z, 0) plus
+ * a log1p term, so no input overflows.  Not checked: inputs are finite.
+ */
+kda_status kda_chunk_prefill_fused_gate(const kda_prefill_desc *desc,
+                                        const void *q, const void *k, const void *v,
+                                        const void *gate_x, const float *A_log,
+                                        const float *dt_bias, const void *beta_x,
+                                        const int32_t *cu_seqlens,
+                                        void *state, const int32_t *state_indices,
+                                        void *final_state, void *o,
+                                        void *workspace, size_t workspace_bytes,
+                                        void *stream);
+
 /* Host-side description of one decode call. */
 typedef struct {
     int32_t batch;        /* B >= 0 requests, one token each                  */
@@ -149,6 +179,21 @@ kda_status kda_recurrent_decode(const kda_decode_desc *desc,
                                 const float *g, const float *beta,
                                 void *state_pool, const int32_t *state_indices,
                                 void *o, void *stream);
+
+/*
+ * One-token decode with the gate activation fused in, as for
+ * kda_chunk_prefill_fused_gate:
+ *   gate_x   [B, hv, dk] (CHANNEL) or [B, hv] (SCALAR), io dtype
+ *   A_log, dt_bias  [hv, dk] (CHANNEL) or [hv] (SCALAR), fp32
+ *   beta_x   [B, hv] io dtype
+ * Everything else is as for kda_recurrent_decode.
+ */
+kda_status kda_recurrent_decode_fused_gate(const kda_decode_desc *desc,
+                                           const void *q, const void *k, const void *v,
+                                           const void *gate_x, const float *A_log,
+                                           const float *dt_bias, const void *beta_x,
+                                           void *state_pool, const int32_t *state_indices,
+                                           void *o, void *stream);
 
 /* Static description of a status code. */
 const char *kda_status_string(kda_status status);

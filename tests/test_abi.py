@@ -134,3 +134,47 @@ def test_decode_errors(L):
     assert decode(L, ddesc(), o=fake(8, 8)) == ALIGN
     assert decode(L, ddesc(), o=fake(6, 1024)) == ALIAS     # o inside the pool
     assert decode(L, ddesc(batch=0), q=None) == OK          # nothing to do
+
+
+def prefill_fused(L, d, **over):
+    args = dict(q=fake(1), k=fake(2), v=fake(3), x=fake(4), A_log=fake(12), dt_bias=fake(13),
+                b=fake(5), cu=fake(6), state=None, idx=None, final=fake(7), o=fake(8), ws=fake(9),
+                wsb=1 << 40)
+    args.update(over)
+    return L.kda_chunk_prefill_fused_gate(ctypes.byref(d), args["q"], args["k"], args["v"], args["x"],
+                                          args["A_log"], args["dt_bias"], args["b"], args["cu"],
+                                          args["state"], args["idx"], args["final"], args["o"],
+                                          args["ws"], args["wsb"], None)
+
+
+def test_prefill_fused_gate_errors(L):
+    assert L.kda_chunk_prefill_fused_gate(None, *([None] * 13), 0, None) == NULL
+    d = desc()
+    assert prefill_fused(L, desc(dk=96)) == UNSUP
+    assert prefill_fused(L, d, x=None) == NULL
+    assert prefill_fused(L, d, A_log=None) == NULL
+    assert prefill_fused(L, d, dt_bias=None) == NULL
+    assert prefill_fused(L, d, b=None) == NULL
+    assert prefill_fused(L, d, A_log=fake(12, 8)) == ALIGN
+    assert prefill_fused(L, d, o=fake(12)) == ALIAS          # o is A_log
+    assert prefill_fused(L, d, o=fake(4, 512)) == ALIAS      # o inside the raw gate input
+    assert prefill_fused(L, d, ws=None) == WS
+
+
+def decode_fused(L, d, **over):
+    args = dict(q=fake(1), k=fake(2), v=fake(3), x=fake(4), A_log=fake(12), dt_bias=fake(13),
+                b=fake(5), pool=fake(6), idx=fake(7), o=fake(8))
+    args.update(over)
+    return L.kda_recurrent_decode_fused_gate(ctypes.byref(d), args["q"], args["k"], args["v"], args["x"],
+                                             args["A_log"], args["dt_bias"], args["b"], args["pool"],
+                                             args["idx"], args["o"], None)
+
+
+def test_decode_fused_gate_errors(L):
+    assert L.kda_recurrent_decode_fused_gate(None, *([None] * 11)) == NULL
+    assert decode_fused(L, ddesc(hv=3)) == SHAPE
+    assert decode_fused(L, ddesc(), A_log=None) == NULL
+    assert decode_fused(L, ddesc(), dt_bias=None) == NULL
+    assert decode_fused(L, ddesc(), dt_bias=fake(13, 4)) == ALIGN
+    assert decode_fused(L, ddesc(), o=fake(13)) == ALIAS     # o is dt_bias
+    assert decode_fused(L, ddesc(batch=0), x=None) == OK
