@@ -232,3 +232,43 @@ def decode_b4096(seed=5, batch=4096, num_slots=4160):
     """Recurrent decode: 4096 one-token requests, Hk=Hv=32, K=V=128, bf16 io,
     realistic gates, fp32 pool of 4160 slots."""
     return make_decode(seed, batch, 32, 32, 128, 128, num_slots)
+
+
+@dataclass
+class MultiDecode:
+    """Multi-token decode: request n owns tokens [cu[n], cu[n+1]) of the packed
+    token arrays (``tok``, a Prefill without states) and pool row indices[n]."""
+    tok: Prefill
+    pool: torch.Tensor
+    indices: torch.Tensor
+    cache_pitch: int
+    meta: dict = field(default_factory=dict)
+
+
+def make_multi_decode(seed, lengths, hk, hv, dk, dv, num_slots, cache_pitch, io="bf16",
+                      gate="realistic", scalar_gate=False, state_dtype="f32", pad=0, scale=1.0):
+    """Draft/verify batch: ``lengths`` tokens per request (list, or (n, lo, hi)),
+    a pool of ``num_slots`` random rows, slot indices drawn without replacement
+    from [0, num_slots - 1) with the last ``pad`` set to -1, and the step pitch
+    of the intermediate-state cache."""
+    tok = make_prefill(seed, lengths, hk, hv, dk, dv, io=io, gate=gate, scalar_gate=scalar_gate,
+                       scale=scale)
+    gen = _gen(seed + 7919)
+    n = tok.num_seqs
+    assert n <= num_slots - 1
+    idx = torch.randperm(num_slots - 1, generator=gen)[:n].to(torch.int32)
+    if pad:
+        idx[n - pad:] = -1
+    pool = torch.empty(num_slots, hv, dv, dk, dtype=DTYPES[state_dtype])
+    for s in range(num_slots):
+        pool[s] = torch.randn(hv, dv, dk, generator=gen) * 0.05
+    return MultiDecode(tok, pool, idx, cache_pitch,
+                       meta=dict(seed=seed, batch=n, hk=hk, hv=hv, dk=dk, dv=dv, io=io,
+                                 state_dtype=state_dtype, num_slots=num_slots, pitch=cache_pitch))
+
+
+def spec_decode_b1024(seed=6, batch=1024, draft=4, num_slots=1088, cache_pitch=8):
+    """Speculative verify step: 1024 requests of 4 tokens (the last accepted
+    token plus 3 drafts), Hk=Hv=32, K=V=128, bf16 io, realistic gates, fp32
+    pool of 1088 slots, intermediate-state cache pitch 8 steps."""
+    return make_multi_decode(seed, [draft] * batch, 32, 32, 128, 128, num_slots, cache_pitch)

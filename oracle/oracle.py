@@ -193,6 +193,48 @@ def prefill_fused_gate(q, k, v, x, A_log, dt_bias, b, cu_seqlens, h0=None, scale
                    h0=h0, scale=scale, want_state=want_state, nthreads=nthreads)
 
 
+def decode_steps(q, k, v, g, beta, cu_seqlens, h0, scale=1.0, nthreads=0):
+    """Multi-token decode (speculative draft / verify) with the state after
+    every token, fp64.
+
+    Request n runs its tokens [cu[n], cu[n+1]) from h0[n].  Returns (o
+    [T, Hv, V], states [T, Hv, V, K]) where states[t] is the state right after
+    token t: the per-step intermediate states a verify step caches so that the
+    state at any accepted draft length can be restored (FLA/MoE shape-limits
+    digest, sglang PR 37317, 实现拆解 item 2 and the key-code snippet: a
+    per-request cache of per-step states whose step pitch is fixed at
+    allocation while the draft count varies from call to call).
+
+    Written as the plain recurrence on every prefix: the state after token j
+    of request n is the final state of the prefix [cu[n], cu[n] + j] run from
+    h0[n] (all prefixes go through ``prefill`` in one batched call)."""
+    cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64)
+    q, k, v = (_f32(x) for x in (q, k, v))
+    g, beta = _f64(g), _f64(beta)
+    h0 = _f32(h0)
+    T = q.shape[0]
+    idx, pcu, ph0 = [], [0], []
+    for n in range(len(cu) - 1):
+        for end in range(cu[n] + 1, cu[n + 1] + 1):
+            idx.extend(range(cu[n], end))
+            pcu.append(len(idx))
+            ph0.append(h0[n])
+    hv, dv, dk = v.shape[1], v.shape[2], q.shape[2]
+    if T == 0:
+        return np.zeros((0, hv, dv)), np.zeros((0, hv, dv, dk))
+    idx = np.asarray(idx)
+    o_all, ht = prefill(q[idx], k[idx], v[idx], g[idx], beta[idx], np.asarray(pcu, np.int32),
+                        h0=np.stack(ph0), scale=scale, nthreads=nthreads)
+    # prefix p ends at token t = idx[pcu[p + 1] - 1]; its last output row is o_t
+    ends = np.asarray(pcu[1:]) - 1
+    order = idx[ends]
+    o = np.zeros((T, hv, dv))
+    states = np.zeros((T, hv, dv, dk))
+    o[order] = o_all[ends]
+    states[order] = ht
+    return o, states
+
+
 def map_slot(idx, num_slots):
     """Padding index -1 (any negative) selects the last (sentinel) slot
     (PR 30169 digest, 实现拆解 item 3 and the wrapper code)."""

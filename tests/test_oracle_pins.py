@@ -298,3 +298,39 @@ def test_decode_is_one_token_prefill(oracle):
         ob, hb = oracle.prefill(d.q[b:b + 1], d.k[b:b + 1], d.v[b:b + 1], d.g[b:b + 1],
                                 d.beta[b:b + 1], np.array([0, 1], np.int32), h0=h0[b:b + 1])
         assert np.array_equal(ob[0], o[b]) and np.array_equal(hb[0], ht[b])
+
+
+def test_decode_steps_transition_form(oracle):
+    """The per-step states of the multi-token decode equal the transition-matrix
+    form applied one token at a time, S_t = (I - b k k^T) D_t S_{t-1} + b k v^T
+    (math orientation K x V), and o_t = scale S_t^T q_t; requests of 1..5
+    tokens (one request empty) with GQA."""
+    inp = W.make_prefill(59, [3, 1, 5, 0, 2], 1, 2, 6, 4, io="f32", gate="realistic", h0="random")
+    o, st = oracle.decode_steps(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, inp.h0, scale=0.8)
+    q, k, v, g, b = (x.double().numpy() for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    cu = inp.cu_seqlens.numpy()
+    for n in range(5):
+        for h in range(2):
+            S = inp.h0[n, h].double().numpy().T
+            for t in range(cu[n], cu[n + 1]):
+                kt = k[t, 0]
+                S = (np.eye(6) - b[t, h] * np.outer(kt, kt)) @ (np.exp(g[t, h])[:, None] * S) \
+                    + b[t, h] * np.outer(kt, v[t, h])
+                np.testing.assert_allclose(st[t, h], S.T, rtol=1e-12, atol=1e-13)
+                np.testing.assert_allclose(o[t, h], 0.8 * S.T @ q[t, 0], rtol=1e-12, atol=1e-13)
+
+
+def test_decode_steps_last_state_is_prefill_final(oracle):
+    """The state after each request's last token is the prefill final state,
+    and one token per request reduces to the one-token decode."""
+    inp = W.make_prefill(60, [4, 2, 7], 2, 4, 8, 8, io="f32", gate="realistic", h0="random")
+    o, st = oracle.decode_steps(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, inp.h0)
+    o2, ht = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=inp.h0)
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+    ends = inp.cu_seqlens.numpy()[1:] - 1
+    np.testing.assert_allclose(st[ends], ht, rtol=1e-12, atol=1e-13)
+    d = W.make_decode(61, 5, 2, 4, 8, 8, num_slots=6)
+    h0 = d.pool[:5]
+    o1, s1 = oracle.decode_steps(d.q, d.k, d.v, d.g, d.beta, np.arange(6, dtype=np.int32), h0)
+    o3, s3 = oracle.decode(d.q, d.k, d.v, d.g, d.beta, h0)
+    assert np.array_equal(o1, o3) and np.array_equal(s1, s3)
