@@ -11,7 +11,9 @@ One step = one pass of the whole path over one batch of synthetic input:
 Inputs are generated on the host (seeded), copied to HBM before timing, and
 stay resident.  After the timed steps the same workloads are passed through
 the fused-gate entry points (raw bf16 gate and beta inputs, activation inside
-the kernels) and reported under "fused_gate".  Prints one JSON line.
+the kernels) and reported under "fused_gate", and a multi-token verify decode
+(1024 requests x 4 tokens with a per-step state cache) is timed and reported
+under "spec_decode".  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 """
@@ -80,6 +82,19 @@ def decode_work(B, hk, hv, dk, dv, gate_bytes=4):
     return B * hv * per + (8 * hv * dk if gate_bytes != 4 else 0)
 
 
+def multi_decode_work(lengths, hk, hv, dk, dv, pitch, update_pool, gate_bytes=2):
+    """Bytes of one multi-token decode call: per (request, head) the fp32 state
+    read once, one fp32 state written per cached step (min(L, pitch) of them),
+    the pool row written back if update_pool; per (token, head) q, k, v, g,
+    beta, o as for decode_work; A_log and dt_bias once."""
+    state = 4 * dk * dv
+    tokens = sum(lengths)
+    per_tok = 2 * dk * 2 * hk / hv + 2 * dv + gate_bytes * (dk + 1) + 2 * dv
+    steps = sum(min(L, pitch) for L in lengths)
+    busy = sum(1 for L in lengths if L > 0)
+    return hv * (busy * state * (2 if update_pool else 1) + steps * state + tokens * per_tok) + 8 * hv * dk
+
+
 def cpu_baseline(pre, dec, reps=5, nreq=1024):
     """The fp64 oracle on the host cores, on a bounded sample of the same
     workload: the full prefill batch (all 16 sequences, all heads; median of
@@ -122,6 +137,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--spec-steps", type=int, default=10,
+                    help="after the timed steps, time this many multi-token verify decodes "
+                         "(1024 requests x 4 tokens, cache pitch 8; 0: skip)")
     ap.add_argument("--fused-gate-steps", type=int, default=10,
                     help="after the timed steps, time this many passes through the fused-gate "
                          "entry points (0: skip)")
@@ -213,6 +231,39 @@ def main():
         fused_dec_ms = sum(e[1].elapsed_time(e[2]) for e in fev[1:]) / fsteps
     finite = all(bool(torch.isfinite(X["pool"]).all().item()) for X in (P, D) if X)
 
+    # multi-token verify decode (speculative decoding), timed on its own
+    spec = None
+    if args.spec_steps > 0 and do_dec:
+        m = W.spec_decode_b1024()
+        t = m.tok
+        S = {n: getattr(t, n).to(dev) for n in ("q", "k", "v", "gx", "A_log", "dt_bias", "bx", "cu_seqlens")}
+        spool, sidx = m.pool.to(dev), m.indices.to(dev)
+        hv_, dv_, dk_ = t.v.shape[1], t.v.shape[2], t.q.shape[2]
+        cache = torch.empty(t.num_seqs, m.cache_pitch, hv_, dv_, dk_, dtype=spool.dtype, device=dev)
+
+        def verify():
+            kda.recurrent_decode_multi_fused_gate(S["q"], S["k"], S["v"], S["gx"], S["A_log"], S["dt_bias"],
+                                                  S["bx"], S["cu_seqlens"], spool, sidx,
+                                                  intermediate_states=cache, update_pool=False)
+        verify()
+        torch.cuda.synchronize()
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.spec_steps)]
+        for e in sev:
+            e[0].record()
+            verify()
+            e[1].record()
+        torch.cuda.synchronize()
+        spec_ms = sum(e[0].elapsed_time(e[1]) for e in sev) / args.spec_steps
+        lens = (t.cu_seqlens[1:] - t.cu_seqlens[:-1]).tolist()
+        sb = multi_decode_work(lens, t.q.shape[1], hv_, dk_, dv_, m.cache_pitch, False)
+        spec = {"workload": "multi-token verify decode: 1024 requests x 4 tokens, Hk=Hv=32, K=V=128, bf16 io, "
+                            "fused gate, fp32 pool 1088 slots read-only, fp32 step cache pitch 8",
+                "steps": args.spec_steps, "ms": spec_ms,
+                "tokens_per_s": sum(lens) / (spec_ms * 1e-3),
+                "alg_bytes_per_launch": sb, "alg_gbs": sb / (spec_ms * 1e-3) / 1e9,
+                "hbm_frac_alg": sb / (spec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del cache, spool
+
     hk, hv, dk, dv = 32, 32, 128, 128
     cu = pre.cu_seqlens.tolist() if do_pre else [0]
     T = cu[-1]
@@ -273,7 +324,7 @@ def main():
                                "+ recurrent decode: B=4096, Hk=Hv=32, K=V=128, fp32 pool 4160 slots" % T,
                    "global_batch": len(cu) - 1, "seq_len": T, "parallelism": "single-gpu"},
         "prefill": prefill, "decode": decode, "roofline": roof, "finite": finite,
-        "fused_gate": fused,
+        "fused_gate": fused, "spec_decode": spec,
     }
     if not args.no_cpu_baseline and do_pre and do_dec:
         out["cpu_baseline"] = cpu_baseline(pre, dec)

@@ -16,6 +16,10 @@ anything else.
     o, final_state = chunk_prefill_fused_gate(q, k, v, x, A_log, dt_bias, b, cu_seqlens, ...)
     o = recurrent_decode_fused_gate(q, k, v, x, A_log, dt_bias, b, state_pool, state_indices)
 
+    # multi-token (speculative verify) decode with a per-step state cache
+    o = recurrent_decode_multi(q, k, v, g, beta, cu_seqlens, state_pool, state_indices,
+                               intermediate_states=cache, update_pool=False)
+
 Layouts (contiguous): q, k [T, Hk, K]; v [T, Hv, V]; g [T, Hv, K] (per-channel
 gate) or [T, Hv] (scalar gate); beta [T, Hv] fp32; states [.., Hv, V, K];
 raw x shaped like g and b like beta, both in the io dtype; A_log, dt_bias
@@ -29,7 +33,8 @@ import os
 import torch
 
 __all__ = ["chunk_prefill", "recurrent_decode", "chunk_prefill_fused_gate",
-           "recurrent_decode_fused_gate", "workspace_size", "library_path", "KdaError"]
+           "recurrent_decode_fused_gate", "recurrent_decode_multi", "recurrent_decode_multi_fused_gate",
+           "workspace_size", "library_path", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -50,6 +55,16 @@ class PrefillDesc(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
                 ("gate", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("num_slots", ctypes.c_int32)]
+
+
+class MultiDecodeDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("hk", ctypes.c_int32), ("hv", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("num_slots", ctypes.c_int32), ("cache_pitch", ctypes.c_int32),
+                ("update_pool", ctypes.c_int32)]
 
 
 class DecodeDesc(ctypes.Structure):
@@ -85,6 +100,10 @@ def lib():
         L.kda_chunk_prefill_fused_gate.argtypes = [ctypes.POINTER(PrefillDesc)] + [_P] * 13 + [ctypes.c_size_t, _P]
         L.kda_recurrent_decode_fused_gate.restype = ctypes.c_int
         L.kda_recurrent_decode_fused_gate.argtypes = [ctypes.POINTER(DecodeDesc)] + [_P] * 11
+        L.kda_recurrent_decode_multi.restype = ctypes.c_int
+        L.kda_recurrent_decode_multi.argtypes = [ctypes.POINTER(MultiDecodeDesc)] + [_P] * 11
+        L.kda_recurrent_decode_multi_fused_gate.restype = ctypes.c_int
+        L.kda_recurrent_decode_multi_fused_gate.argtypes = [ctypes.POINTER(MultiDecodeDesc)] + [_P] * 13
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_version.restype = ctypes.c_int32
@@ -245,3 +264,61 @@ def recurrent_decode_fused_gate(q, k, v, gate_x, A_log, dt_bias, beta_x, state_p
     """recurrent_decode with the gate activation computed inside the kernel."""
     gate = _gate_args(q, None, None, (gate_x, A_log, dt_bias, beta_x))
     return _decode(q, k, v, gate, state_pool, state_indices, scale, True)
+
+
+def _cache_pitch(cache, n, hv, dv, dk, dtype):
+    """Step pitch of an intermediate-state cache [N', steps, Hv, V, K]: taken
+    from stride(0), the per-request pitch fixed at allocation, so a view that
+    keeps only the first few steps of a larger cache is accepted."""
+    if cache is None:
+        return 0
+    if cache.dtype != dtype:
+        raise ValueError("intermediate_states must have the pool's dtype %s" % dtype)
+    if cache.dim() != 5 or tuple(cache.shape[2:]) != (hv, dv, dk) or cache.shape[0] < n:
+        raise ValueError("intermediate_states must be [>= N, steps, Hv, V, K]")
+    unit = hv * dv * dk
+    st = cache.stride()
+    if st[1:] != (unit, dv * dk, dk, 1) or st[0] % unit != 0 or st[0] // unit < cache.shape[1]:
+        raise ValueError("intermediate_states must be contiguous within each request")
+    return st[0] // unit
+
+
+def _decode_multi(q, k, v, gate, cu_seqlens, state_pool, state_indices, cache, update_pool, scale, raw):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(state_pool, "state_pool", None, 4)
+    _need(state_indices, "state_indices", torch.int32, 1)
+    T, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1
+    pitch = _cache_pitch(cache, N, hv, dv, dk, state_pool.dtype)
+    desc = MultiDecodeDesc(N, T, hk, hv, dk, dv, _io_dtype(q), _DT[state_pool.dtype],
+                           GATE_SCALAR if gate[0].dim() == 2 else GATE_CHANNEL, float(scale),
+                           state_pool.shape[0], pitch, 1 if update_pool else 0)
+    o = torch.empty(T, hv, dv, dtype=q.dtype, device=q.device)
+    fn = lib().kda_recurrent_decode_multi_fused_gate if raw else lib().kda_recurrent_decode_multi
+    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate), _ptr(cu_seqlens),
+              _ptr(state_pool), _ptr(state_indices), _ptr(cache) if pitch else None, _ptr(o),
+              _stream(q.device)))
+    return o
+
+
+def recurrent_decode_multi(q, k, v, g, beta, cu_seqlens, state_pool, state_indices, *,
+                           intermediate_states=None, update_pool=True, scale=1.0):
+    """Multi-token decode (speculative verify): request n runs tokens
+    [cu[n], cu[n+1]) from pool row state_indices[n]; the state after its j-th
+    token goes to intermediate_states[n, j] ([N', steps, Hv, V, K], pitch from
+    stride(0); steps beyond the pitch are not cached).  With update_pool the
+    last state is written back to the pool row.  Returns o [T, Hv, V]."""
+    return _decode_multi(q, k, v, _gate_args(q, g, beta, None), cu_seqlens, state_pool, state_indices,
+                         intermediate_states, update_pool, scale, False)
+
+
+def recurrent_decode_multi_fused_gate(q, k, v, gate_x, A_log, dt_bias, beta_x, cu_seqlens, state_pool,
+                                      state_indices, *, intermediate_states=None, update_pool=True,
+                                      scale=1.0):
+    """recurrent_decode_multi with the gate activation computed inside the kernel."""
+    gate = _gate_args(q, None, None, (gate_x, A_log, dt_bias, beta_x))
+    return _decode_multi(q, k, v, gate, cu_seqlens, state_pool, state_indices, intermediate_states,
+                         update_pool, scale, True)

@@ -184,6 +184,80 @@ kda_status decode_impl(const kda_decode_desc *d, const void *q, const void *k, c
     return hip_status(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+kda_status check_multi_desc(const kda_multi_decode_desc *d) {
+    if (!d) return KDA_ERR_NULL;
+    if (d->batch < 0 || d->total_tokens < 0 || d->hk <= 0 || d->hv <= 0 || d->dk <= 0 || d->dv <= 0 ||
+        d->hv % d->hk != 0 || d->num_slots <= 0 || d->cache_pitch < 0)
+        return KDA_ERR_SHAPE;
+    if (!dim_ok(d->dk) || !dim_ok(d->dv) || !dtype_ok(d->io_dtype) || !dtype_ok(d->state_dtype) ||
+        !gate_ok(d->gate))
+        return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+kda_status multi_decode_impl(const kda_multi_decode_desc *d, const void *q, const void *k, const void *v,
+                             const GateIn &gi, const int32_t *cu_seqlens, void *state_pool,
+                             const int32_t *state_indices, void *cache, void *o, void *stream) {
+    kda_status st = check_multi_desc(d);
+    if (st != KDA_OK) return st;
+    if (d->batch == 0) return KDA_OK;
+    if (!cu_seqlens || !state_pool || !state_indices) return KDA_ERR_NULL;
+    if (d->cache_pitch > 0 && !cache) return KDA_ERR_NULL;
+    const long T = d->total_tokens;
+    if (T > 0 && (!q || !k || !v || !gi.g || !gi.beta || !o)) return KDA_ERR_NULL;
+    if (T > 0 && gi.raw && (!gi.A_log || !gi.dt_bias)) return KDA_ERR_NULL;
+    if (d->cache_pitch == 0) cache = nullptr;
+    const void *ptrs[] = {q, k, v, gi.g, gi.beta, gi.A_log, gi.dt_bias, cu_seqlens, state_pool, state_indices,
+                          cache, o};
+    for (const void *p : ptrs)
+        if (p && !aligned(p)) return KDA_ERR_ALIGN;
+    const size_t isz = io_size(d->io_dtype), ssz = io_size(d->state_dtype), gsz = gi.raw ? isz : 4;
+    const size_t gw = d->gate == KDA_GATE_SCALAR ? 1 : (size_t)d->dk, N = d->batch;
+    const size_t unit = (size_t)d->hv * d->dv * d->dk * ssz;   // one state row of all heads
+    const size_t o_b = (size_t)T * d->hv * d->dv * isz;
+    const size_t par_b = gi.raw ? (size_t)d->hv * gw * 4 : 0;
+    const size_t cache_b = cache ? N * (size_t)d->cache_pitch * unit : 0;
+    struct R { const void *p; size_t n; } ins[] = {
+        {q, (size_t)T * d->hk * d->dk * isz}, {k, (size_t)T * d->hk * d->dk * isz}, {v, o_b},
+        {gi.g, (size_t)T * d->hv * gw * gsz}, {gi.beta, (size_t)T * d->hv * gsz}, {gi.A_log, par_b},
+        {gi.dt_bias, par_b}, {cu_seqlens, (N + 1) * 4}, {state_pool, (size_t)d->num_slots * unit},
+        {state_indices, N * 4}};
+    for (const R &r : ins) {
+        if (overlap(o, o_b, r.p, r.n)) return KDA_ERR_ALIAS;
+        if (overlap(cache, cache_b, r.p, r.n)) return KDA_ERR_ALIAS;
+    }
+    if (overlap(cache, cache_b, o, o_b)) return KDA_ERR_ALIAS;
+    if (T == 0) return KDA_OK;   // every request is empty: nothing is read or written
+
+    int dev = 0, max_x = 0, max_y = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess)
+        return KDA_ERR_HIP;
+    const long xdim = (long)d->hv * (d->dv / kda::decode_tile(d->dv));
+    if ((long)d->batch > max_y || xdim > max_x) return KDA_ERR_UNSUPPORTED;
+
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.state = state_pool;
+    if (gi.raw) {
+        a.gx = gi.g; a.bx = gi.beta; a.A_log = gi.A_log; a.dt_bias = gi.dt_bias;
+    } else {
+        a.g = static_cast<const float *>(gi.g); a.beta = static_cast<const float *>(gi.beta);
+    }
+    a.indices = state_indices; a.o = o;
+    a.batch = d->batch; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
+    a.num_slots = d->num_slots; a.scale = d->scale;
+    a.io_bf16 = d->io_dtype == KDA_BF16;
+    a.state_bf16 = d->state_dtype == KDA_BF16;
+    a.scalar_gate = d->gate == KDA_GATE_SCALAR;
+    a.raw_gate = gi.raw;
+    a.cu_seqlens = cu_seqlens;
+    a.cache = cache;
+    a.cache_pitch = d->cache_pitch;
+    a.update_pool = d->update_pool != 0;
+    return hip_status(kda::launch_decode_multi(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -242,6 +316,27 @@ kda_status kda_recurrent_decode_fused_gate(const kda_decode_desc *d, const void 
                                            const int32_t *state_indices, void *o, void *stream) {
     const GateIn gi{gate_x, beta_x, A_log, dt_bias, true};
     return decode_impl(d, q, k, v, gi, state_pool, state_indices, o, stream);
+}
+
+kda_status kda_recurrent_decode_multi(const kda_multi_decode_desc *d, const void *q, const void *k,
+                                      const void *v, const float *g, const float *beta,
+                                      const int32_t *cu_seqlens, void *state_pool,
+                                      const int32_t *state_indices, void *intermediate_states, void *o,
+                                      void *stream) {
+    const GateIn gi{g, beta, nullptr, nullptr, false};
+    return multi_decode_impl(d, q, k, v, gi, cu_seqlens, state_pool, state_indices, intermediate_states, o,
+                             stream);
+}
+
+kda_status kda_recurrent_decode_multi_fused_gate(const kda_multi_decode_desc *d, const void *q, const void *k,
+                                                 const void *v, const void *gate_x, const float *A_log,
+                                                 const float *dt_bias, const void *beta_x,
+                                                 const int32_t *cu_seqlens, void *state_pool,
+                                                 const int32_t *state_indices, void *intermediate_states,
+                                                 void *o, void *stream) {
+    const GateIn gi{gate_x, beta_x, A_log, dt_bias, true};
+    return multi_decode_impl(d, q, k, v, gi, cu_seqlens, state_pool, state_indices, intermediate_states, o,
+                             stream);
 }
 
 }  // extern "C"

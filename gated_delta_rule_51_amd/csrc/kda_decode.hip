@@ -1,4 +1,7 @@
-// One-token recurrent decode of the gated delta rule against a state pool.
+// Recurrent decode of the gated delta rule against a state pool: one token per
+// request (decode_kernel), or a short run of tokens per request with the state
+// after every token cached (multi_decode_kernel, the verify step of
+// speculative decoding).
 //
 // Per (value tile, request b, value head h) one workgroup streams the BV rows
 // of the stored state pool[slot(b), h] ([V, K], K contiguous), applies
@@ -19,37 +22,27 @@
 
 namespace kda {
 
-template <int DK, int BV, typename IO, typename ST, bool SCALAR, bool RAW, bool NT>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-    constexpr int VEC = (sizeof(ST) == 4) ? 4 : 8;  // state elements per 16 B
-    constexpr int LPR = DK / VEC;                    // lanes per stored row
-    constexpr int RPP = 256 / LPR;                   // rows per pass
-    constexpr int NP = (BV + RPP - 1) / RPP;         // passes
+// Thread layout over one workgroup's BV stored rows: LPR lanes per row, each
+// holding VEC consecutive channels (16 bytes of state); NP passes of RPP rows.
+template <int DK, int BV, typename ST> struct RowTile {
+    static constexpr int VEC = (sizeof(ST) == 4) ? 4 : 8;  // state elements per 16 B
+    static constexpr int LPR = DK / VEC;                    // lanes per stored row
+    static constexpr int RPP = 256 / LPR;                   // rows per pass
+    static constexpr int NP = (BV + RPP - 1) / RPP;         // passes
     static_assert(DK % VEC == 0 && LPR <= 64, "tile");
+};
 
-    const int tid = threadIdx.x;
-    const int cg = tid % LPR;
-    const int r0 = tid / LPR;
-    constexpr int NT_MAX = 128 / BV;
-    const int nt = a.dv / BV;   // value tiles per head (1 when BV = dv)
-    const int b = blockIdx.y;
-    const int h = NT_MAX == 1 ? (int)blockIdx.x : (int)blockIdx.x / nt;
-    const int j0 = NT_MAX == 1 ? 0 : ((int)blockIdx.x % nt) * BV;
-    const int hk_idx = h / (a.hv / a.hk);
-
-    int slot = a.indices[b];
-    if (slot < 0) slot = a.num_slots - 1;
-    ST *st = reinterpret_cast<ST *>(a.state) +
-             (((long)slot * a.hv + h) * a.dv + j0) * (long)DK;
-
-    // Issue every state load first.
-    float s[NP][VEC];
+// Load this thread's part of the BV rows at `st` (row stride DK) into s.
+template <int DK, int BV, typename ST, bool NT>
+__device__ __forceinline__ void load_rows(const ST *st, int r0, int cg,
+                                          float (&s)[RowTile<DK, BV, ST>::NP][RowTile<DK, BV, ST>::VEC]) {
+    using R = RowTile<DK, BV, ST>;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int row = r0 + p * RPP;
+    for (int p = 0; p < R::NP; ++p) {
+        const int row = r0 + p * R::RPP;
         if (row < BV) {
-            const ST *src = st + (long)row * DK + cg * VEC;
-            if constexpr (VEC == 4) {
+            const ST *src = st + (long)row * DK + cg * R::VEC;
+            if constexpr (R::VEC == 4) {
                 f32x4 x = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src)) : load4(src);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s[p][i] = x[i];
@@ -64,88 +57,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             }
         }
     }
+}
 
-    const int c0 = cg * VEC;
-    float dec[VEC], kk[VEC], qq[VEC];
-    const IO *kp = reinterpret_cast<const IO *>(a.k) + ((long)b * a.hk + hk_idx) * DK + c0;
-    const IO *qp = reinterpret_cast<const IO *>(a.q) + ((long)b * a.hk + hk_idx) * DK + c0;
+// Store this thread's part of the rows to `st` (bf16 storage rounds to nearest even).
+template <int DK, int BV, typename ST, bool NT>
+__device__ __forceinline__ void store_rows(ST *st, int r0, int cg,
+                                           const float (&s)[RowTile<DK, BV, ST>::NP][RowTile<DK, BV, ST>::VEC]) {
+    using R = RowTile<DK, BV, ST>;
 #pragma unroll
-    for (int i = 0; i < VEC; i += 4) {
-        f32x4 x = load4(kp + i), y = load4(qp + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            kk[i + e] = x[e];
-            qq[i + e] = y[e];
-        }
-    }
-    float beta;
-    if constexpr (RAW) {
-        // raw gate x (io dtype) activated here: exp(g), g = -exp(A_log) softplus(x + dt_bias)
-        const IO *xp = reinterpret_cast<const IO *>(a.gx);
-        if constexpr (SCALAR) {
-            const float x = io_traits<IO>::load(xp, (long)b * a.hv + h);
-            const float d = gate_decay((x + a.dt_bias[h]) * kLog2e, exp_f(a.A_log[h]));
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) dec[i] = d;
-        } else {
-#pragma unroll
-            for (int i = 0; i < VEC; i += 4) {
-                const f32x4 x = load4(xp + ((long)b * a.hv + h) * DK + c0 + i);
-                const f32x4 al = *reinterpret_cast<const f32x4 *>(a.A_log + (long)h * DK + c0 + i);
-                const f32x4 db = *reinterpret_cast<const f32x4 *>(a.dt_bias + (long)h * DK + c0 + i);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dec[i + e] = gate_decay((x[e] + db[e]) * kLog2e, exp_f(al[e]));
-            }
-        }
-        beta = sigmoid_f(io_traits<IO>::load(reinterpret_cast<const IO *>(a.bx), (long)b * a.hv + h));
-    } else {
-        if constexpr (SCALAR) {
-            const float d = exp_f(a.g[(long)b * a.hv + h]);
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) dec[i] = d;
-        } else {
-            const float *gp = a.g + ((long)b * a.hv + h) * DK + c0;
-#pragma unroll
-            for (int i = 0; i < VEC; i += 4) {
-                f32x4 x = *reinterpret_cast<const f32x4 *>(gp + i);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dec[i + e] = exp_f(x[e]);
-            }
-        }
-        beta = a.beta[(long)b * a.hv + h];
-    }
-    const IO *vp = reinterpret_cast<const IO *>(a.v) + ((long)b * a.hv + h) * a.dv + j0;
-    IO *op = reinterpret_cast<IO *>(a.o) + ((long)b * a.hv + h) * a.dv + j0;
-
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int row = r0 + p * RPP;
+    for (int p = 0; p < R::NP; ++p) {
+        const int row = r0 + p * R::RPP;
         if (row < BV) {
-            float pk = 0.f;
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                s[p][i] *= dec[i];
-                pk += s[p][i] * kk[i];
-            }
-            pk = group_sum<LPR>(pk);
-            const float u = beta * (io_traits<IO>::load(vp, row) - pk);
-            float pq = 0.f;
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                s[p][i] += kk[i] * u;
-                pq += s[p][i] * qq[i];
-            }
-            pq = group_sum<LPR>(pq);
-            if (cg == 0) io_traits<IO>::store(op, row, a.scale * pq);
-        }
-    }
-
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int row = r0 + p * RPP;
-        if (row < BV) {
-            ST *dst = st + (long)row * DK + cg * VEC;
-            if constexpr (VEC == 4) {
+            ST *dst = st + (long)row * DK + cg * R::VEC;
+            if constexpr (R::VEC == 4) {
                 f32x4 x;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) x[i] = s[p][i];
@@ -162,35 +86,211 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
 }
 
+// The per-token inputs of one (token t, value head h) for channels c0 .. c0+VEC-1:
+// k, q, the decay factors exp(g) and beta (activated here from raw inputs if RAW).
+template <int DK, int VEC, typename IO, bool SCALAR, bool RAW>
+__device__ __forceinline__ void token_inputs(const DecodeArgs &a, long t, int h, int hk_idx, int c0,
+                                             float (&kk)[VEC], float (&qq)[VEC], float (&dec)[VEC],
+                                             float &beta) {
+    const IO *kp = reinterpret_cast<const IO *>(a.k) + (t * a.hk + hk_idx) * DK + c0;
+    const IO *qp = reinterpret_cast<const IO *>(a.q) + (t * a.hk + hk_idx) * DK + c0;
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4) {
+        f32x4 x = load4(kp + i), y = load4(qp + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kk[i + e] = x[e];
+            qq[i + e] = y[e];
+        }
+    }
+    if constexpr (RAW) {
+        // raw gate x (io dtype) activated here: exp(g), g = -exp(A_log) softplus(x + dt_bias)
+        const IO *xp = reinterpret_cast<const IO *>(a.gx);
+        if constexpr (SCALAR) {
+            const float x = io_traits<IO>::load(xp, t * a.hv + h);
+            const float d = gate_decay((x + a.dt_bias[h]) * kLog2e, exp_f(a.A_log[h]));
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) dec[i] = d;
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; i += 4) {
+                const f32x4 x = load4(xp + (t * a.hv + h) * DK + c0 + i);
+                const f32x4 al = *reinterpret_cast<const f32x4 *>(a.A_log + (long)h * DK + c0 + i);
+                const f32x4 db = *reinterpret_cast<const f32x4 *>(a.dt_bias + (long)h * DK + c0 + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dec[i + e] = gate_decay((x[e] + db[e]) * kLog2e, exp_f(al[e]));
+            }
+        }
+        beta = sigmoid_f(io_traits<IO>::load(reinterpret_cast<const IO *>(a.bx), t * a.hv + h));
+    } else {
+        if constexpr (SCALAR) {
+            const float d = exp_f(a.g[t * a.hv + h]);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) dec[i] = d;
+        } else {
+            const float *gp = a.g + (t * a.hv + h) * DK + c0;
+#pragma unroll
+            for (int i = 0; i < VEC; i += 4) {
+                f32x4 x = *reinterpret_cast<const f32x4 *>(gp + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dec[i + e] = exp_f(x[e]);
+            }
+        }
+        beta = a.beta[t * a.hv + h];
+    }
+}
+
+// One token applied to this thread's rows: decay, residual against v, rank-1
+// write, read-out; lane cg == 0 of each row writes o.
+template <int DK, int BV, typename IO, typename ST>
+__device__ __forceinline__ void token_update(const IO *vp, IO *op, float scale, int r0, int cg,
+                                             float (&s)[RowTile<DK, BV, ST>::NP][RowTile<DK, BV, ST>::VEC],
+                                             const float (&kk)[RowTile<DK, BV, ST>::VEC],
+                                             const float (&qq)[RowTile<DK, BV, ST>::VEC],
+                                             const float (&dec)[RowTile<DK, BV, ST>::VEC], float beta) {
+    using R = RowTile<DK, BV, ST>;
+#pragma unroll
+    for (int p = 0; p < R::NP; ++p) {
+        const int row = r0 + p * R::RPP;
+        if (row < BV) {
+            float pk = 0.f;
+#pragma unroll
+            for (int i = 0; i < R::VEC; ++i) {
+                s[p][i] *= dec[i];
+                pk += s[p][i] * kk[i];
+            }
+            pk = group_sum<R::LPR>(pk);
+            const float u = beta * (io_traits<IO>::load(vp, row) - pk);
+            float pq = 0.f;
+#pragma unroll
+            for (int i = 0; i < R::VEC; ++i) {
+                s[p][i] += kk[i] * u;
+                pq += s[p][i] * qq[i];
+            }
+            pq = group_sum<R::LPR>(pq);
+            if (cg == 0) io_traits<IO>::store(op, row, scale * pq);
+        }
+    }
+}
+
+template <int DK, int BV, typename IO, typename ST, bool SCALAR, bool RAW, bool NT>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+    using R = RowTile<DK, BV, ST>;
+    const int tid = threadIdx.x;
+    const int cg = tid % R::LPR;
+    const int r0 = tid / R::LPR;
+    constexpr int NT_MAX = 128 / BV;
+    const int nt = a.dv / BV;   // value tiles per head (1 when BV = dv)
+    const int b = blockIdx.y;
+    const int h = NT_MAX == 1 ? (int)blockIdx.x : (int)blockIdx.x / nt;
+    const int j0 = NT_MAX == 1 ? 0 : ((int)blockIdx.x % nt) * BV;
+    const int hk_idx = h / (a.hv / a.hk);
+
+    int slot = a.indices[b];
+    if (slot < 0) slot = a.num_slots - 1;
+    ST *st = reinterpret_cast<ST *>(a.state) + (((long)slot * a.hv + h) * a.dv + j0) * (long)DK;
+
+    // Issue every state load first.
+    float s[R::NP][R::VEC];
+    load_rows<DK, BV, ST, NT>(st, r0, cg, s);
+
+    float dec[R::VEC], kk[R::VEC], qq[R::VEC], beta;
+    token_inputs<DK, R::VEC, IO, SCALAR, RAW>(a, b, h, hk_idx, cg * R::VEC, kk, qq, dec, beta);
+    const IO *vp = reinterpret_cast<const IO *>(a.v) + ((long)b * a.hv + h) * a.dv + j0;
+    IO *op = reinterpret_cast<IO *>(a.o) + ((long)b * a.hv + h) * a.dv + j0;
+    token_update<DK, BV, IO, ST>(vp, op, a.scale, r0, cg, s, kk, qq, dec, beta);
+
+    store_rows<DK, BV, ST, NT>(st, r0, cg, s);
+}
+
+// Multi-token decode: request b runs its tokens [cu[b], cu[b+1]) one after
+// the other with the state held in registers, writes o for each, caches the
+// state after step j at cache[b * pitch + j] (j < pitch; the pitch is the
+// per-request step count the cache was allocated with, sglang PR 37317
+// digest, 实现拆解 item 2), and with update_pool writes the last state back to
+// the pool row.  A request with no tokens writes nothing.
+template <int DK, int BV, typename IO, typename ST, bool SCALAR, bool RAW>
+__global__ __launch_bounds__(256) void multi_decode_kernel(DecodeArgs a) {
+    using R = RowTile<DK, BV, ST>;
+    const int tid = threadIdx.x;
+    const int cg = tid % R::LPR;
+    const int r0 = tid / R::LPR;
+    constexpr int NT_MAX = 128 / BV;
+    const int nt = a.dv / BV;
+    const int b = blockIdx.y;
+    const int h = NT_MAX == 1 ? (int)blockIdx.x : (int)blockIdx.x / nt;
+    const int j0 = NT_MAX == 1 ? 0 : ((int)blockIdx.x % nt) * BV;
+    const int hk_idx = h / (a.hv / a.hk);
+    const int t0 = a.cu_seqlens[b], t1 = a.cu_seqlens[b + 1];
+    if (t1 <= t0) return;
+
+    int slot = a.indices[b];
+    if (slot < 0) slot = a.num_slots - 1;
+    ST *st = reinterpret_cast<ST *>(a.state) + (((long)slot * a.hv + h) * a.dv + j0) * (long)DK;
+    float s[R::NP][R::VEC];
+    load_rows<DK, BV, ST, true>(st, r0, cg, s);
+
+    const long step_elems = (long)a.hv * a.dv * DK;   // one cached step of one request
+    ST *cache = reinterpret_cast<ST *>(a.cache);
+    for (int t = t0; t < t1; ++t) {
+        float dec[R::VEC], kk[R::VEC], qq[R::VEC], beta;
+        token_inputs<DK, R::VEC, IO, SCALAR, RAW>(a, t, h, hk_idx, cg * R::VEC, kk, qq, dec, beta);
+        const IO *vp = reinterpret_cast<const IO *>(a.v) + ((long)t * a.hv + h) * a.dv + j0;
+        IO *op = reinterpret_cast<IO *>(a.o) + ((long)t * a.hv + h) * a.dv + j0;
+        token_update<DK, BV, IO, ST>(vp, op, a.scale, r0, cg, s, kk, qq, dec, beta);
+        const int j = t - t0;
+        if (cache != nullptr && j < a.cache_pitch)
+            store_rows<DK, BV, ST, true>(cache + ((long)b * a.cache_pitch + j) * step_elems +
+                                             ((long)h * a.dv + j0) * DK, r0, cg, s);
+    }
+    if (a.update_pool) store_rows<DK, BV, ST, true>(st, r0, cg, s);
+}
+
 template <int DK, int BV, typename IO, typename ST, bool SCALAR>
-static hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
+static hipError_t launch_t(const DecodeArgs &a, bool multi, hipStream_t stream) {
     // The state block is touched once per call: stream it past the caches.
     dim3 grid(a.hv * (a.dv / BV), a.batch);
-    if (a.raw_gate)
-        decode_kernel<DK, BV, IO, ST, SCALAR, true, true><<<grid, 256, 0, stream>>>(a);
-    else
-        decode_kernel<DK, BV, IO, ST, SCALAR, false, true><<<grid, 256, 0, stream>>>(a);
+    if (multi) {
+        if (a.raw_gate)
+            multi_decode_kernel<DK, BV, IO, ST, SCALAR, true><<<grid, 256, 0, stream>>>(a);
+        else
+            multi_decode_kernel<DK, BV, IO, ST, SCALAR, false><<<grid, 256, 0, stream>>>(a);
+    } else {
+        if (a.raw_gate)
+            decode_kernel<DK, BV, IO, ST, SCALAR, true, true><<<grid, 256, 0, stream>>>(a);
+        else
+            decode_kernel<DK, BV, IO, ST, SCALAR, false, true><<<grid, 256, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 
 template <int DK, int BV, typename IO, typename ST>
-static hipError_t launch_g(const DecodeArgs &a, hipStream_t s) {
-    return a.scalar_gate ? launch_t<DK, BV, IO, ST, true>(a, s) : launch_t<DK, BV, IO, ST, false>(a, s);
+static hipError_t launch_g(const DecodeArgs &a, bool m, hipStream_t s) {
+    return a.scalar_gate ? launch_t<DK, BV, IO, ST, true>(a, m, s) : launch_t<DK, BV, IO, ST, false>(a, m, s);
 }
 template <int DK, int BV, typename IO>
-static hipError_t launch_s(const DecodeArgs &a, hipStream_t s) {
-    return a.state_bf16 ? launch_g<DK, BV, IO, bf16>(a, s) : launch_g<DK, BV, IO, float>(a, s);
+static hipError_t launch_s(const DecodeArgs &a, bool m, hipStream_t s) {
+    return a.state_bf16 ? launch_g<DK, BV, IO, bf16>(a, m, s) : launch_g<DK, BV, IO, float>(a, m, s);
 }
 template <int DK, int BV>
-static hipError_t launch_i(const DecodeArgs &a, hipStream_t s) {
-    return a.io_bf16 ? launch_s<DK, BV, bf16>(a, s) : launch_s<DK, BV, float>(a, s);
+static hipError_t launch_i(const DecodeArgs &a, bool m, hipStream_t s) {
+    return a.io_bf16 ? launch_s<DK, BV, bf16>(a, m, s) : launch_s<DK, BV, float>(a, m, s);
 }
 template <int DK>
-static hipError_t launch_v(const DecodeArgs &a, int bv, hipStream_t s) {
+static hipError_t launch_v(const DecodeArgs &a, int bv, bool m, hipStream_t s) {
     switch (bv) {
-    case 32: return launch_i<DK, 32>(a, s);
-    case 64: return launch_i<DK, 64>(a, s);
-    default: return launch_i<DK, 128>(a, s);
+    case 32: return launch_i<DK, 32>(a, m, s);
+    case 64: return launch_i<DK, 64>(a, m, s);
+    default: return launch_i<DK, 128>(a, m, s);
+    }
+}
+
+static hipError_t launch_any(const DecodeArgs &a, bool multi, hipStream_t stream) {
+    const int bv = decode_tile(a.dv);
+    switch (a.dk) {
+    case 32: return launch_v<32>(a, bv, multi, stream);
+    case 64: return launch_v<64>(a, bv, multi, stream);
+    default: return launch_v<128>(a, bv, multi, stream);
     }
 }
 
@@ -198,13 +298,8 @@ static hipError_t launch_v(const DecodeArgs &a, int bv, hipStream_t s) {
 // (K = V = 128, B = 4096, Hv = 32: 3.0 ms vs 3.3 ms with 64-row tiles).
 int decode_tile(int dv) { return dv < 128 ? dv : 128; }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-    const int bv = decode_tile(a.dv);
-    switch (a.dk) {
-    case 32: return launch_v<32>(a, bv, stream);
-    case 64: return launch_v<64>(a, bv, stream);
-    default: return launch_v<128>(a, bv, stream);
-    }
-}
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) { return launch_any(a, false, stream); }
+
+hipError_t launch_decode_multi(const DecodeArgs &a, hipStream_t stream) { return launch_any(a, true, stream); }
 
 }  // namespace kda

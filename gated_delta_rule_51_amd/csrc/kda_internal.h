@@ -18,9 +18,16 @@ struct DecodeArgs {
     int batch, hk, hv, dk, dv, num_slots;
     float scale;
     bool io_bf16, state_bf16, scalar_gate, raw_gate;
+    // multi-token decode only: request n owns tokens [cu_seqlens[n], cu_seqlens[n+1]);
+    // the state after its step j goes to cache[n * cache_pitch + j] when j < cache_pitch
+    const int32_t *cu_seqlens;
+    void *cache;
+    int cache_pitch;
+    bool update_pool;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_multi(const DecodeArgs &a, hipStream_t stream);
 int decode_tile(int dv);
 
 // Chunked prefill.  Chunk size and the chunk-slot bound are fixed here.

@@ -195,6 +195,62 @@ kda_status kda_recurrent_decode_fused_gate(const kda_decode_desc *desc,
                                            void *state_pool, const int32_t *state_indices,
                                            void *o, void *stream);
 
+/* Host-side description of one multi-token decode call. */
+typedef struct {
+    int32_t batch;        /* N >= 0 requests                                   */
+    int32_t total_tokens; /* T >= 0, equals cu_seqlens[N] on the device         */
+    int32_t hk, hv, dk, dv;
+    int32_t io_dtype, state_dtype, gate;
+    float scale;
+    int32_t num_slots;    /* pool rows                                          */
+    int32_t cache_pitch;  /* steps per request in the intermediate-state cache,
+                             or 0 for no cache                                  */
+    int32_t update_pool;  /* nonzero: write each request's last state back to
+                             its pool row; 0: the pool is only read             */
+} kda_multi_decode_desc;
+
+/*
+ * Multi-token recurrent decode: the verify step of speculative decoding.
+ * Request n runs its tokens [cu_seqlens[n], cu_seqlens[n+1]) in order from
+ * the state in pool row state_indices[n] (negative: the last row), writes o
+ * for every token and caches the state after its j-th token (j = 0, 1, ...)
+ * at intermediate_states[n * cache_pitch + j] for j < cache_pitch, so that the
+ * state at any accepted draft length can be restored.  The pitch is the step
+ * count the cache was allocated with, not the current number of drafts, which
+ * may change from call to call (FLA/MoE shape-limits digest, sglang PR 37317,
+ * 实现拆解 item 2: the cache stride is derived from the allocation's
+ * per-request pitch).
+ *   q, k  [T, hk, dk] io dtype;  v [T, hv, dv] io dtype
+ *   g     [T, hv, dk] (CHANNEL) or [T, hv] (SCALAR) fp32;  beta [T, hv] fp32
+ *   cu_seqlens     [N + 1] int32 (device)
+ *   state_pool     [num_slots, hv, dv, dk] state dtype
+ *   state_indices  [N] int32
+ *   intermediate_states  [N, cache_pitch, hv, dv, dk] state dtype, or NULL
+ *                  when cache_pitch is 0; steps at or beyond cache_pitch are
+ *                  not cached; must not overlap any other argument
+ *   o     [T, hv, dv] io dtype
+ * The grid is (hv x dv / tile, N) as for kda_recurrent_decode.  A request
+ * with no tokens writes nothing.  Not checked (preconditions, besides those of
+ * kda_chunk_prefill): indices of requests with update_pool set are unique.
+ */
+kda_status kda_recurrent_decode_multi(const kda_multi_decode_desc *desc,
+                                      const void *q, const void *k, const void *v,
+                                      const float *g, const float *beta,
+                                      const int32_t *cu_seqlens,
+                                      void *state_pool, const int32_t *state_indices,
+                                      void *intermediate_states, void *o, void *stream);
+
+/* kda_recurrent_decode_multi with the gate activation fused in, as for
+ * kda_chunk_prefill_fused_gate (gate_x [T, hv, dk] or [T, hv] and beta_x
+ * [T, hv] in the io dtype; A_log, dt_bias [hv, dk] or [hv] fp32). */
+kda_status kda_recurrent_decode_multi_fused_gate(const kda_multi_decode_desc *desc,
+                                                 const void *q, const void *k, const void *v,
+                                                 const void *gate_x, const float *A_log,
+                                                 const float *dt_bias, const void *beta_x,
+                                                 const int32_t *cu_seqlens,
+                                                 void *state_pool, const int32_t *state_indices,
+                                                 void *intermediate_states, void *o, void *stream);
+
 /* Static description of a status code. */
 const char *kda_status_string(kda_status status);
 

@@ -178,3 +178,35 @@ def test_decode_fused_gate_errors(L):
     assert decode_fused(L, ddesc(), dt_bias=fake(13, 4)) == ALIGN
     assert decode_fused(L, ddesc(), o=fake(13)) == ALIAS     # o is dt_bias
     assert decode_fused(L, ddesc(batch=0), x=None) == OK
+
+
+def mdesc(**kw):
+    d = dict(batch=4, total_tokens=12, hk=2, hv=4, dk=128, dv=128, io_dtype=1, state_dtype=0, gate=0,
+             scale=1.0, num_slots=16, cache_pitch=4, update_pool=1)
+    d.update(kw)
+    return kda.MultiDecodeDesc(**d)
+
+
+def multi(L, d, **over):
+    args = dict(q=fake(1), k=fake(2), v=fake(3), g=fake(4), beta=fake(5), cu=fake(9), pool=fake(6),
+                idx=fake(7), cache=fake(10), o=fake(8))
+    args.update(over)
+    return L.kda_recurrent_decode_multi(ctypes.byref(d), args["q"], args["k"], args["v"], args["g"],
+                                        args["beta"], args["cu"], args["pool"], args["idx"], args["cache"],
+                                        args["o"], None)
+
+
+def test_multi_decode_errors(L):
+    assert L.kda_recurrent_decode_multi(None, *([None] * 11)) == NULL
+    assert L.kda_recurrent_decode_multi_fused_gate(None, *([None] * 13)) == NULL
+    assert multi(L, mdesc(hv=3)) == SHAPE
+    assert multi(L, mdesc(cache_pitch=-1)) == SHAPE
+    assert multi(L, mdesc(total_tokens=-1)) == SHAPE
+    assert multi(L, mdesc(dk=48)) == UNSUP
+    assert multi(L, mdesc(), cu=None) == NULL
+    assert multi(L, mdesc(), cache=None) == NULL                 # pitch > 0 needs a cache
+    assert multi(L, mdesc(), cache=fake(10, 4)) == ALIGN
+    assert multi(L, mdesc(), cache=fake(6, 1 << 20)) == ALIAS    # cache inside the pool
+    assert multi(L, mdesc(), o=fake(10, 4096)) == ALIAS          # o inside the cache
+    assert multi(L, mdesc(batch=0), q=None) == OK
+    assert multi(L, mdesc(total_tokens=0), q=None, o=None, cache=fake(10)) == OK
