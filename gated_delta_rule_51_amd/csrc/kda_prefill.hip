@@ -850,11 +850,15 @@ __device__ __forceinline__ size_t uniform_off(size_t x) {
 
 // Per-wave part of one (sequence, head) chain; UW selects the role (U wave or
 // output wave).  Both roles pass the same barriers in the same order.
-template <bool UW, int DK, int DV, typename IO, typename ST>
-__device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w, StateSmem<DK, DV, IO> &sm,
-                                            int n, int h, int wave, int lane) {
+template <bool UW, int DK, int DV, int DVW, typename IO, typename ST>
+__device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w, StateSmem<DK, DVW, IO> &sm,
+                                            int n, int h, int j0, int wave, int lane) {
+    // This workgroup owns value columns j0 .. j0 + DVW - 1 of the chain (the
+    // columns of S, U and O never mix, so a chain may be split over several
+    // workgroups by columns); memory strides use the full width DV.
     constexpr int KK = DK / 32;               // k-steps over key channels
-    constexpr int CT = DV / 16;               // value column tiles
+    constexpr int CT = DVW / 16;              // value column tiles of this workgroup
+    constexpr int CTF = DV / 16;              // value column tiles of the full state
     constexpr int R = DK / 16;                // key row tiles of the state
     constexpr int NST = R * CT;               // state tiles
     constexpr int NTW = NST >= 8 ? NST / 8 : 1;   // state tiles per wave (one key row tile)
@@ -884,7 +888,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
                                     : nullptr;
 #pragma unroll
         for (int c = 0; c < NTW; ++c)
-            S[c] = (sin && swave) ? load_state4<ST>(sin + (size_t)(16 * (ct0 + c) + m) * DK + 16 * kr + 4 * kq)
+            S[c] = (sin && swave) ? load_state4<ST>(sin + (size_t)(j0 + 16 * (ct0 + c) + m) * DK + 16 * kr + 4 * kq)
                                   : zero4();
     }
 
@@ -918,7 +922,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) Xa[kk] = ld8(Xg, lo16 + kk * 1024u);
         if constexpr (UW) {
-            const _Float16 *Ug = w.Ut + uniform_off(sh * C * DV + (size_t)rt * CT * 256);
+            const _Float16 *Ug = w.Ut + uniform_off(sh * C * DV + ((size_t)rt * CTF + j0 / 16) * 256);
             const unsigned lo8 = lane_off(8u);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) Ua[ct] = ld4(Ug, lo8 + ct * 512u);
@@ -1013,8 +1017,8 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             // buffer's range is the valid rows of this tile, so the stores of
             // rows past the sequence end are dropped by the hardware range
             // check and no store is under a branch.
-            constexpr int EPV = 16 / sizeof(IO), VPR = DV / EPV;   // elements per vector, vectors per row
-            char *ob = reinterpret_cast<char *>(og + uniform_off(((size_t)(t0 + 16 * rt) * a.hv + h) * DV));
+            constexpr int EPV = 16 / sizeof(IO), VPR = DVW / EPV;  // elements per vector, vectors per row
+            char *ob = reinterpret_cast<char *>(og + uniform_off(((size_t)(t0 + 16 * rt) * a.hv + h) * DV + j0));
             const int orow = a.hv * DV * (int)sizeof(IO);
             const int nrec = __builtin_amdgcn_readfirstlane(max(0, min(16, L - 16 * rt)) * orow);   // bytes
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(ob, 0, nrec, kBufferWord3);
@@ -1045,23 +1049,32 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
         ST *sout = reinterpret_cast<ST *>(a.state_out) + ((size_t)row_out * a.hv + h) * DV * DK;
 #pragma unroll
         for (int c = 0; c < NTW; ++c)
-            store_state4(sout + (size_t)(16 * (ct0 + c) + m) * DK + 16 * kr + 4 * kq, S[c]);
+            store_state4(sout + (size_t)(j0 + 16 * (ct0 + c) + m) * DK + 16 * kr + 4 * kq, S[c]);
     }
 }
 
-template <int DK, int DV, typename IO, typename ST>
+template <int DK, int DV, int DVW, typename IO, typename ST>
 __global__ __launch_bounds__(NTS, 4) void state_kernel(PrefillArgs a, Work w) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    StateSmem<DK, DV, IO> &sm = *reinterpret_cast<StateSmem<DK, DV, IO> *>(smem_raw);
-    // (sequence rank, head), rank-major: the longest sequences come first
-    const int unit = blockIdx.x;
-    const int h = unit % a.hv, rank = unit / a.hv;
+    StateSmem<DK, DVW, IO> &sm = *reinterpret_cast<StateSmem<DK, DVW, IO> *>(smem_raw);
+    // (sequence rank, head) chains, rank-major: the longest sequences come
+    // first.  With NSPLIT > 1 the NSPLIT column parts of a chain get block ids
+    // kXcd apart inside one group of kXcd chains: the ids go round robin over
+    // the XCDs, so the parts share one XCD (and its L2) and start together.
+    constexpr int NSPLIT = DV / DVW;
+    int chain = blockIdx.x, part = 0;
+    if constexpr (NSPLIT > 1) {
+        const int grp = blockIdx.x / (kXcd * NSPLIT), r = blockIdx.x % (kXcd * NSPLIT);
+        part = r / kXcd;
+        chain = grp * kXcd + r % kXcd;
+    }
+    const int h = chain % a.hv, rank = chain / a.hv;
     if (rank >= a.num_seqs) return;
     const int n = w.seq_order[rank];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (wave < 4) state_chain<true, DK, DV, IO, ST>(a, w, sm, n, h, wave, lane);    // U waves
-    else state_chain<false, DK, DV, IO, ST>(a, w, sm, n, h, wave, lane);   // output waves
+    if (wave < 4) state_chain<true, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);    // U waves
+    else state_chain<false, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);   // output waves
 }
 
 // ---------------------------------------------------------------------------
@@ -1079,14 +1092,27 @@ hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DK, int DV, int DVW, typename IO, typename ST>
+hipError_t launch_state_w(PrefillArgs &a, Work &w, hipStream_t s) {
+    // 1-D grid over (sequence rank, head) chains, rank-major, times the column parts
+    const size_t smem = sizeof(StateSmem<DK, DVW, IO>);
+    auto kern = state_kernel<DK, DV, DVW, IO, ST>;
+    hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    const long chains = (long)a.hv * a.num_seqs;
+    const long blocks = DV == DVW ? chains : (chains + kXcd - 1) / kXcd * kXcd * (DV / DVW);
+    kern<<<dim3((unsigned)blocks), NTS, smem, s>>>(a, w);
+    return hipGetLastError();
+}
+
 template <int DK, int DV, typename IO, typename ST>
 hipError_t launch_state_st(PrefillArgs &a, Work &w, hipStream_t s) {
-    // 1-D grid over (sequence rank, head) pairs, rank-major
-    const size_t smem = sizeof(StateSmem<DK, DV, IO>);
-    auto kern = state_kernel<DK, DV, IO, ST>;
-    hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    kern<<<dim3((unsigned)((long)a.hv * a.num_seqs)), NTS, smem, s>>>(a, w);
-    return hipGetLastError();
+    // Split a chain's 128 value columns over two workgroups while the chains
+    // alone do not fill the device twice over: the per-chunk critical path of
+    // a chain halves, and the longest chains set the kernel's end.
+    if constexpr (DV == 128) {
+        if (state_split(a.hv, a.num_seqs, DV) > 1) return launch_state_w<DK, DV, DV / 2, IO, ST>(a, w, s);
+    }
+    return launch_state_w<DK, DV, DV, IO, ST>(a, w, s);
 }
 
 template <int DK, int DV, typename IO>

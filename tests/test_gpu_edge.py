@@ -7,7 +7,9 @@ against the fp64 oracle through the C ABI:
   token's own contribution survives;
 * wide GQA (one key head for eight value heads);
 * many short sequences, including more than the meta kernel ranks by length
-  (the natural order is kept beyond that count) and more than one scan block.
+  (the natural order is kept beyond that count) and more than one scan block;
+* 128 value columns with more (sequence, head) chains than the state kernel
+  splits by columns, so the unsplit path runs too.
 """
 import numpy as np
 import pytest
@@ -73,3 +75,13 @@ def test_many_short_sequences(K, oracle, n):
     lens[n // 2] = 70   # one sequence with two chunks
     inp = W.make_prefill(75 + n, lens, 1, 2, 64, 64, h0="random", scale=64 ** -0.5)
     run_and_check(K, oracle, inp, "N=%d short" % n)
+
+
+def test_unsplit_state_chains(K, oracle):
+    """600 sequences x 2 heads = 1200 chains with V = 128: above the count for
+    which the state kernel splits each chain's value columns over two
+    workgroups, so every chain runs whole in one workgroup."""
+    g = torch.Generator().manual_seed(76)
+    lens = torch.randint(0, 80, (600,), generator=g).tolist()
+    inp = W.make_prefill(76, lens, 1, 2, 128, 128, gate="realistic", h0="random")
+    run_and_check(K, oracle, inp, "1200 chains, V=128")
