@@ -16,6 +16,9 @@ anything else.
     o, final_state = chunk_prefill_fused_gate(q, k, v, x, A_log, dt_bias, b, cu_seqlens, ...)
     o = recurrent_decode_fused_gate(q, k, v, x, A_log, dt_bias, b, state_pool, state_indices)
 
+    # decode from one packed [q | k | v] row per request
+    o = recurrent_decode_packed(qkv, g, beta, state_pool, state_indices, hk=..., hv=..., dk=..., dv=...)
+
     # multi-token (speculative verify) decode with a per-step state cache
     o = recurrent_decode_multi(q, k, v, g, beta, cu_seqlens, state_pool, state_indices,
                                intermediate_states=cache, update_pool=False)
@@ -34,6 +37,7 @@ import torch
 
 __all__ = ["chunk_prefill", "recurrent_decode", "chunk_prefill_fused_gate",
            "recurrent_decode_fused_gate", "recurrent_decode_multi", "recurrent_decode_multi_fused_gate",
+           "recurrent_decode_packed", "recurrent_decode_packed_fused_gate",
            "workspace_size", "library_path", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +104,10 @@ def lib():
         L.kda_chunk_prefill_fused_gate.argtypes = [ctypes.POINTER(PrefillDesc)] + [_P] * 13 + [ctypes.c_size_t, _P]
         L.kda_recurrent_decode_fused_gate.restype = ctypes.c_int
         L.kda_recurrent_decode_fused_gate.argtypes = [ctypes.POINTER(DecodeDesc)] + [_P] * 11
+        L.kda_recurrent_decode_packed.restype = ctypes.c_int
+        L.kda_recurrent_decode_packed.argtypes = [ctypes.POINTER(DecodeDesc)] + [_P] * 7
+        L.kda_recurrent_decode_packed_fused_gate.restype = ctypes.c_int
+        L.kda_recurrent_decode_packed_fused_gate.argtypes = [ctypes.POINTER(DecodeDesc)] + [_P] * 9
         L.kda_recurrent_decode_multi.restype = ctypes.c_int
         L.kda_recurrent_decode_multi.argtypes = [ctypes.POINTER(MultiDecodeDesc)] + [_P] * 11
         L.kda_recurrent_decode_multi_fused_gate.restype = ctypes.c_int
@@ -322,3 +330,38 @@ def recurrent_decode_multi_fused_gate(q, k, v, gate_x, A_log, dt_bias, beta_x, c
     gate = _gate_args(q, None, None, (gate_x, A_log, dt_bias, beta_x))
     return _decode_multi(q, k, v, gate, cu_seqlens, state_pool, state_indices, intermediate_states,
                          update_pool, scale, True)
+
+
+def _decode_packed(qkv, gate, state_pool, state_indices, hk, hv, dk, dv, scale, raw):
+    if qkv.dim() != 2 or qkv.shape[1] != 2 * hk * dk + hv * dv:
+        raise ValueError("qkv must be [B, 2 hk dk + hv dv]")
+    _need(qkv, "qkv", None, 2)
+    _need(state_pool, "state_pool", None, 4)
+    _need(state_indices, "state_indices", torch.int32, 1)
+    B = qkv.shape[0]
+    desc = DecodeDesc(B, hk, hv, dk, dv, _io_dtype(qkv), _DT[state_pool.dtype],
+                      GATE_SCALAR if gate[0].dim() == 2 else GATE_CHANNEL, float(scale), state_pool.shape[0])
+    o = torch.empty(B, hv, dv, dtype=qkv.dtype, device=qkv.device)
+    fn = lib().kda_recurrent_decode_packed_fused_gate if raw else lib().kda_recurrent_decode_packed
+    _check(fn(ctypes.byref(desc), _ptr(qkv), *(_ptr(t) for t in gate), _ptr(state_pool), _ptr(state_indices),
+              _ptr(o), _stream(qkv.device)))
+    return o
+
+
+def recurrent_decode_packed(qkv, g, beta, state_pool, state_indices, *, hk, hv, dk, dv, scale=1.0):
+    """recurrent_decode with q, k, v read from one packed row per request:
+    qkv [B, 2 hk dk + hv dv] = [q | k | v].  Returns o [B, Hv, V]."""
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32, 2)
+    return _decode_packed(qkv, (g, beta), state_pool, state_indices, hk, hv, dk, dv, scale, False)
+
+
+def recurrent_decode_packed_fused_gate(qkv, gate_x, A_log, dt_bias, beta_x, state_pool, state_indices, *,
+                                       hk, hv, dk, dv, scale=1.0):
+    """recurrent_decode_packed with the gate activation computed inside the kernel."""
+    _need(gate_x, "gate_x", qkv.dtype)
+    _need(beta_x, "beta_x", qkv.dtype, 2)
+    _need(A_log, "A_log", torch.float32, gate_x.dim() - 1)
+    _need(dt_bias, "dt_bias", torch.float32, gate_x.dim() - 1)
+    return _decode_packed(qkv, (gate_x, A_log, dt_bias, beta_x), state_pool, state_indices, hk, hv, dk, dv,
+                          scale, True)

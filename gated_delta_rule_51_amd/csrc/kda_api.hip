@@ -136,12 +136,19 @@ kda_status prefill_impl(const kda_prefill_desc *d, const void *q, const void *k,
     return hip_status(kda::launch_prefill(a, workspace, static_cast<hipStream_t>(stream)));
 }
 
+// packed: q points at one [q | k | v] row per request (k and v are offsets into it).
 kda_status decode_impl(const kda_decode_desc *d, const void *q, const void *k, const void *v,
                        const GateIn &gi, void *state_pool, const int32_t *state_indices, void *o,
-                       void *stream) {
+                       void *stream, bool packed = false) {
     kda_status st = check_decode_desc(d);
     if (st != KDA_OK) return st;
     if (d->batch == 0) return KDA_OK;
+    const size_t isz0 = io_size(d->io_dtype);
+    const long qk_w = (long)d->hk * d->dk, v_w = (long)d->hv * d->dv;
+    if (packed && q) {
+        k = static_cast<const char *>(q) + qk_w * isz0;
+        v = static_cast<const char *>(q) + 2 * qk_w * isz0;
+    }
     if (!q || !k || !v || !gi.g || !gi.beta || !state_pool || !state_indices || !o) return KDA_ERR_NULL;
     if (gi.raw && (!gi.A_log || !gi.dt_bias)) return KDA_ERR_NULL;
     const void *ptrs[] = {q, k, v, gi.g, gi.beta, gi.A_log, gi.dt_bias, state_pool, state_indices, o};
@@ -151,8 +158,10 @@ kda_status decode_impl(const kda_decode_desc *d, const void *q, const void *k, c
     const size_t gw = d->gate == KDA_GATE_SCALAR ? 1 : (size_t)d->dk;
     const size_t o_b = B * d->hv * d->dv * isz;
     const size_t par_b = gi.raw ? (size_t)d->hv * gw * 4 : 0;
+    const size_t qkv_b = packed ? B * (size_t)(2 * qk_w + v_w) * isz : 0;
     struct R { const void *p; size_t n; } ins[] = {
-        {q, B * d->hk * d->dk * isz}, {k, B * d->hk * d->dk * isz}, {v, o_b},
+        {q, packed ? qkv_b : B * d->hk * d->dk * isz}, {k, packed ? 0 : B * d->hk * d->dk * isz},
+        {v, packed ? 0 : o_b},
         {gi.g, B * d->hv * gw * gsz}, {gi.beta, B * d->hv * gsz}, {gi.A_log, par_b}, {gi.dt_bias, par_b},
         {state_pool, (size_t)d->num_slots * d->hv * d->dv * d->dk * io_size(d->state_dtype)},
         {state_indices, B * 4}};
@@ -182,6 +191,8 @@ kda_status decode_impl(const kda_decode_desc *d, const void *q, const void *k, c
     a.state_bf16 = d->state_dtype == KDA_BF16;
     a.scalar_gate = d->gate == KDA_GATE_SCALAR;
     a.raw_gate = gi.raw;
+    a.qk_stride = packed ? 2 * qk_w + v_w : qk_w;
+    a.v_stride = packed ? 2 * qk_w + v_w : v_w;
     return hip_status(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -252,6 +263,8 @@ kda_status multi_decode_impl(const kda_multi_decode_desc *d, const void *q, cons
     a.state_bf16 = d->state_dtype == KDA_BF16;
     a.scalar_gate = d->gate == KDA_GATE_SCALAR;
     a.raw_gate = gi.raw;
+    a.qk_stride = (long)d->hk * d->dk;
+    a.v_stride = (long)d->hv * d->dv;
     a.cu_seqlens = cu_seqlens;
     a.cache = cache;
     a.cache_pitch = d->cache_pitch;
@@ -317,6 +330,21 @@ kda_status kda_recurrent_decode_fused_gate(const kda_decode_desc *d, const void 
                                            const int32_t *state_indices, void *o, void *stream) {
     const GateIn gi{gate_x, beta_x, A_log, dt_bias, true};
     return decode_impl(d, q, k, v, gi, state_pool, state_indices, o, stream);
+}
+
+kda_status kda_recurrent_decode_packed(const kda_decode_desc *d, const void *qkv, const float *g,
+                                       const float *beta, void *state_pool, const int32_t *state_indices,
+                                       void *o, void *stream) {
+    const GateIn gi{g, beta, nullptr, nullptr, false};
+    return decode_impl(d, qkv, nullptr, nullptr, gi, state_pool, state_indices, o, stream, true);
+}
+
+kda_status kda_recurrent_decode_packed_fused_gate(const kda_decode_desc *d, const void *qkv,
+                                                  const void *gate_x, const float *A_log,
+                                                  const float *dt_bias, const void *beta_x, void *state_pool,
+                                                  const int32_t *state_indices, void *o, void *stream) {
+    const GateIn gi{gate_x, beta_x, A_log, dt_bias, true};
+    return decode_impl(d, qkv, nullptr, nullptr, gi, state_pool, state_indices, o, stream, true);
 }
 
 kda_status kda_recurrent_decode_multi(const kda_multi_decode_desc *d, const void *q, const void *k,

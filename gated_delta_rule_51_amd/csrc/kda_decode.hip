@@ -92,8 +92,8 @@ template <int DK, int VEC, typename IO, bool SCALAR, bool RAW>
 __device__ __forceinline__ void token_inputs(const DecodeArgs &a, long t, int h, int hk_idx, int c0,
                                              float (&kk)[VEC], float (&qq)[VEC], float (&dec)[VEC],
                                              float &beta) {
-    const IO *kp = reinterpret_cast<const IO *>(a.k) + (t * a.hk + hk_idx) * DK + c0;
-    const IO *qp = reinterpret_cast<const IO *>(a.q) + (t * a.hk + hk_idx) * DK + c0;
+    const IO *kp = reinterpret_cast<const IO *>(a.k) + t * a.qk_stride + hk_idx * DK + c0;
+    const IO *qp = reinterpret_cast<const IO *>(a.q) + t * a.qk_stride + hk_idx * DK + c0;
 #pragma unroll
     for (int i = 0; i < VEC; i += 4) {
         f32x4 x = load4(kp + i), y = load4(qp + i);
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     float dec[R::VEC], kk[R::VEC], qq[R::VEC], beta;
     token_inputs<DK, R::VEC, IO, SCALAR, RAW>(a, b, h, hk_idx, cg * R::VEC, kk, qq, dec, beta);
-    const IO *vp = reinterpret_cast<const IO *>(a.v) + ((long)b * a.hv + h) * a.dv + j0;
+    const IO *vp = reinterpret_cast<const IO *>(a.v) + (long)b * a.v_stride + (long)h * a.dv + j0;
     IO *op = reinterpret_cast<IO *>(a.o) + ((long)b * a.hv + h) * a.dv + j0;
     token_update<DK, BV, IO, ST>(vp, op, a.scale, r0, cg, s, kk, qq, dec, beta);
 
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void multi_decode_kernel(DecodeArgs a) {
     for (int t = t0; t < t1; ++t) {
         float dec[R::VEC], kk[R::VEC], qq[R::VEC], beta;
         token_inputs<DK, R::VEC, IO, SCALAR, RAW>(a, t, h, hk_idx, cg * R::VEC, kk, qq, dec, beta);
-        const IO *vp = reinterpret_cast<const IO *>(a.v) + ((long)t * a.hv + h) * a.dv + j0;
+        const IO *vp = reinterpret_cast<const IO *>(a.v) + (long)t * a.v_stride + (long)h * a.dv + j0;
         IO *op = reinterpret_cast<IO *>(a.o) + ((long)t * a.hv + h) * a.dv + j0;
         token_update<DK, BV, IO, ST>(vp, op, a.scale, r0, cg, s, kk, qq, dec, beta);
         const int j = t - t0;

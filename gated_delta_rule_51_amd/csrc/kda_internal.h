@@ -18,6 +18,9 @@ struct DecodeArgs {
     int batch, hk, hv, dk, dv, num_slots;
     float scale;
     bool io_bf16, state_bf16, scalar_gate, raw_gate;
+    // token row strides (elements) of q, k (same stride) and v: hk * dk and hv * dv
+    // for separate tensors, 2 hk dk + hv dv for one packed [q | k | v] row per token
+    long qk_stride, v_stride;
     // multi-token decode only: request n owns tokens [cu_seqlens[n], cu_seqlens[n+1]);
     // the state after its step j goes to cache[n * cache_pitch + j] when j < cache_pitch
     const int32_t *cu_seqlens;

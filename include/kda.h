@@ -34,6 +34,10 @@
  *     aligned pointers, workspace size, aliasing rules, grid limits) and are
  *     reported as a status; nothing is launched when a check fails.  A launch
  *     failure is reported as KDA_ERR_HIP.  Nothing prints, aborts or throws.
+ *   - Sizes come from the descriptor only: an array may hold more rows than
+ *     the call describes (a batch padded to a captured size), and rows past
+ *     the described count are never read (the KDA prefill digest, sglang
+ *     PR 27488, 实现拆解 item 3, trims padded g and beta to q's token count).
  *   - Not checked (preconditions): device index values lie in [-1, slots-1]
  *     and are unique apart from -1; g is finite and <= 0; cu_seqlens is
  *     non-decreasing with cu[0] = 0 and cu[N] = total_tokens.
@@ -194,6 +198,25 @@ kda_status kda_recurrent_decode_fused_gate(const kda_decode_desc *desc,
                                            const float *dt_bias, const void *beta_x,
                                            void *state_pool, const int32_t *state_indices,
                                            void *o, void *stream);
+
+/*
+ * kda_recurrent_decode / kda_recurrent_decode_fused_gate with q, k and v read
+ * from one packed row per request: qkv [B, 2 hk dk + hv dv] in the io dtype,
+ * each row holding q [hk, dk], then k [hk, dk], then v [hv, dv] (the layout of
+ * a fused q/k/v input projection; the FLA/MoE shape-limits digest, sglang
+ * PR 37317, names the packed KDA decode kernel but does not print its layout,
+ * so this concatenation order is a reading).  Gates, pool, indices, o and the
+ * errors are as for the unpacked calls; qkv must not overlap o.
+ */
+kda_status kda_recurrent_decode_packed(const kda_decode_desc *desc, const void *qkv,
+                                       const float *g, const float *beta,
+                                       void *state_pool, const int32_t *state_indices,
+                                       void *o, void *stream);
+kda_status kda_recurrent_decode_packed_fused_gate(const kda_decode_desc *desc, const void *qkv,
+                                                  const void *gate_x, const float *A_log,
+                                                  const float *dt_bias, const void *beta_x,
+                                                  void *state_pool, const int32_t *state_indices,
+                                                  void *o, void *stream);
 
 /* Host-side description of one multi-token decode call. */
 typedef struct {

@@ -210,3 +210,16 @@ def test_multi_decode_errors(L):
     assert multi(L, mdesc(), o=fake(10, 4096)) == ALIAS          # o inside the cache
     assert multi(L, mdesc(batch=0), q=None) == OK
     assert multi(L, mdesc(total_tokens=0), q=None, o=None, cache=fake(10)) == OK
+
+
+def test_packed_decode_errors(L):
+    assert L.kda_recurrent_decode_packed(None, *([None] * 7)) == NULL
+    assert L.kda_recurrent_decode_packed_fused_gate(None, *([None] * 9)) == NULL
+    d = ddesc()
+    args = [fake(1), fake(4), fake(5), fake(6), fake(7), fake(8), None]
+    bad = list(args); bad[0] = None
+    assert L.kda_recurrent_decode_packed(ctypes.byref(d), *bad) == NULL
+    bad = list(args); bad[5] = fake(1, 4096)                      # o inside the packed rows
+    assert L.kda_recurrent_decode_packed(ctypes.byref(d), *bad) == ALIAS
+    bad = list(args); bad[0] = fake(1, 8)
+    assert L.kda_recurrent_decode_packed(ctypes.byref(d), *bad) == ALIGN
