@@ -85,3 +85,27 @@ def test_unsplit_state_chains(K, oracle):
     lens = torch.randint(0, 80, (600,), generator=g).tolist()
     inp = W.make_prefill(76, lens, 1, 2, 128, 128, gate="realistic", h0="random")
     run_and_check(K, oracle, inp, "1200 chains, V=128")
+
+
+def test_large_token_count(K, oracle):
+    """131,072 tokens (one sequence of 100,000) x 32 heads, K = V = 128: input
+    tensors of 1 GB and a 4.5 GB workspace, so every byte offset past 2^32 is
+    exercised.  Two heads of every sequence are checked against the oracle
+    (the heads do not interact; with Hk = Hv the head slice is exact)."""
+    say("generating 131072-token prefill, 32 heads")
+    inp = W.make_prefill(77, [100000, 20000, 11072], 32, 32, 128, 128, gate="realistic", h0="random")
+    o, ht = K.chunk_prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                            dev(inp.cu_seqlens), initial_state=dev(inp.h0), scale=inp.scale)
+    torch.cuda.synchronize()
+    heads = [0, 17]
+    og = host(o[:, heads])
+    hg = host(ht[:, heads])
+    del o, ht
+    sel = lambda x: x[:, heads].contiguous()
+    o_ref, ht_ref = oracle.prefill(sel(inp.q), sel(inp.k), sel(inp.v), sel(inp.g), sel(inp.beta),
+                                   inp.cu_seqlens, h0=sel(inp.h0), scale=inp.scale)
+    assert np.isfinite(og).all() and np.isfinite(hg).all()
+    e_o, e_s = max_abs(og, o_ref), rel_l2(hg, ht_ref)
+    say("T=131072 heads %s: o max-abs %.3e  state rel-L2 %.3e" % (heads, e_o, e_s))
+    assert e_o <= O_MAXABS
+    assert e_s <= STATE_REL_F32
