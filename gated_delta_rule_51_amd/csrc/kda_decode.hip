@@ -232,9 +232,12 @@ __global__ __launch_bounds__(256) void multi_decode_kernel(DecodeArgs a) {
 
     const long step_elems = (long)a.hv * a.dv * DK;   // one cached step of one request
     ST *cache = reinterpret_cast<ST *>(a.cache);
+    float dec[R::VEC], kk[R::VEC], qq[R::VEC], beta;
+    token_inputs<DK, R::VEC, IO, SCALAR, RAW>(a, t0, h, hk_idx, cg * R::VEC, kk, qq, dec, beta);
     for (int t = t0; t < t1; ++t) {
-        float dec[R::VEC], kk[R::VEC], qq[R::VEC], beta;
-        token_inputs<DK, R::VEC, IO, SCALAR, RAW>(a, t, h, hk_idx, cg * R::VEC, kk, qq, dec, beta);
+        // next token's inputs first (the last token reloads itself)
+        float dec2[R::VEC], kk2[R::VEC], qq2[R::VEC], beta2;
+        token_inputs<DK, R::VEC, IO, SCALAR, RAW>(a, min(t + 1, t1 - 1), h, hk_idx, cg * R::VEC, kk2, qq2, dec2, beta2);
         const IO *vp = reinterpret_cast<const IO *>(a.v) + (long)t * a.v_stride + (long)h * a.dv + j0;
         IO *op = reinterpret_cast<IO *>(a.o) + ((long)t * a.hv + h) * a.dv + j0;
         token_update<DK, BV, IO, ST>(vp, op, a.scale, r0, cg, s, kk, qq, dec, beta);
@@ -242,6 +245,9 @@ __global__ __launch_bounds__(256) void multi_decode_kernel(DecodeArgs a) {
         if (cache != nullptr && j < a.cache_pitch)
             store_rows<DK, BV, ST, true>(cache + ((long)b * a.cache_pitch + j) * step_elems +
                                              ((long)h * a.dv + j0) * DK, r0, cg, s);
+#pragma unroll
+        for (int i = 0; i < R::VEC; ++i) { dec[i] = dec2[i]; kk[i] = kk2[i]; qq[i] = qq2[i]; }
+        beta = beta2;
     }
     if (a.update_pool) store_rows<DK, BV, ST, true>(st, r0, cg, s);
 }
