@@ -150,8 +150,9 @@ def main():
                          "reference for FETCH_SIZE / WRITE_SIZE counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the KDA path has no cross-GPU step to time "
-              "(see the sharding note in DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: (sequence, head) and (request, head) units are "
+              "independent, so more GPUs would each run this same path on their own heads or "
+              "sequences with no cross-GPU step to time; use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

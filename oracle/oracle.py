@@ -19,7 +19,7 @@ Contents
 
 Sources (the pages never print the recurrence; see ``kda_oracle.c``):
   * sglang PR 27488 digest (KDA SM100 CuteDSL prefill): section 功能与动机
-    (per-channel decay gate; outputs judged against a token-by-token
+    (per-channel decay gate; outputs compared with a token-by-token
     baseline), section 实现拆解 (chunk size 64; KKT inverse + U/W step; the
     per-chunk cumsum of the gate).
   * sglang PR 30169 digest (pool-state I/O fused into the state kernel):
