@@ -52,11 +52,8 @@ struct PrefillArgs {
 };
 
 // Column parts per (sequence, head) chain of the state kernel: 2 for 128
-// value columns while there are at most kStateSplitMaxChains chains, else 1.
-constexpr long kStateSplitMaxChains = 1024;
-inline int state_split(int hv, int num_seqs, int dv) {
-    return dv == 128 && (long)hv * num_seqs <= kStateSplitMaxChains ? 2 : 1;
-}
+// value columns, else 1.
+inline int state_split(int dv) { return dv == 128 ? 2 : 1; }
 
 size_t prefill_workspace_bytes(int num_seqs, int total_tokens, int hv, int dk, int dv);
 hipError_t launch_prefill(PrefillArgs &a, void *workspace, hipStream_t stream);

@@ -22,11 +22,12 @@
 // Kernels (all on the caller's stream, no host synchronisation):
 //   meta   : chunk map (sequence, local chunk) per chunk slot, from cu_seqlens
 //   intra  : per (chunk, value head): gate factors, A and M on fp16 MFMA,
-//            T = (I + A)^-1 by blocked inversion on fp32 MFMA, W and Ut on
-//            fp16 MFMA; writes W, Ut, M, Q*exp(G), (K*exp(G_last-G))^T and
-//            exp(G_last) to the workspace
+//            T = (I + A)^-1 by blocked inversion on fp32 MFMA, W on fp16
+//            MFMA; writes W, T diag(beta), M, Q*exp(G), (K*exp(G_last-G))^T
+//            and exp(G_last) to the workspace (it never reads v)
 //   state  : per (value tile, sequence, value head), sequential over chunks:
-//            U = Ut - W S, O, state update; reads h0 and writes the final state
+//            Ut = (T diag(beta)) V from the v rows it streams once, U = Ut - W S,
+//            O, state update; reads h0 and writes the final state
 //            at the sequence's dense row or pool slot (sglang PR 30169 digest,
 //            实现拆解 item 1), a negative slot meaning the last pool row.
 //
@@ -59,36 +60,13 @@ __device__ __forceinline__ int insert_bit(int m, int pos, int v) {
     return ((m >> pos) << (pos + 1)) | (v << pos) | (m & ((1 << pos) - 1));
 }
 
-// Load 8 consecutive io elements as fp16 (exact for bf16 inputs in range).
-template <typename IO> __device__ __forceinline__ f16x8 load8_f16(const IO *p);
-template <> __device__ __forceinline__ f16x8 load8_f16<float>(const float *p) {
-    f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
-    f16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[i] = (_Float16)a[i];
-        r[4 + i] = (_Float16)b[i];
-    }
-    return r;
-}
-template <> __device__ __forceinline__ f16x8 load8_f16<bf16>(const bf16 *p) {
-    u32x4 w = *reinterpret_cast<const u32x4 *>(p);
-    f16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[2 * i] = (_Float16)__uint_as_float(w[i] << 16);
-        r[2 * i + 1] = (_Float16)__uint_as_float(w[i] & 0xffff0000u);
-    }
-    return r;
-}
-
 __device__ __forceinline__ f16x8 lds8(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 
 // ---------------------------------------------------------------------------
 // Workspace layout (per chunk slot s and value head h; all offsets 256-aligned)
 // ---------------------------------------------------------------------------
 struct Layout {
-    size_t chunk_map, chunk_off, seq_order, W, Ut, M, QG, KLt, GL, total;
+    size_t chunk_map, chunk_off, seq_order, W, Tb, M, QG, KLt, GL, total;
     int slots;
 };
 
@@ -104,7 +82,7 @@ __host__ inline Layout make_layout(int num_seqs, int total_tokens, int hv, int d
     l.chunk_off = o; o = align256(o + (size_t)(num_seqs + 1) * 4);
     l.seq_order = o; o = align256(o + (size_t)num_seqs * 4);
     l.W = o;   o = align256(o + per * C * dk * 2);
-    l.Ut = o;  o = align256(o + per * C * dv * 2);
+    l.Tb = o;  o = align256(o + per * C * C * 2);
     l.M = o;   o = align256(o + per * C * C * 2);
     l.QG = o;  o = align256(o + per * C * dk * 2);
     l.KLt = o; o = align256(o + per * dk * C * 2);
@@ -117,7 +95,7 @@ struct Work {
     int2 *chunk_map;       // [slots] (seq, local chunk) or (-1, -1)
     int32_t *chunk_off;    // [N + 1] first chunk slot of each sequence
     int32_t *seq_order;    // [N] sequences by decreasing length (state-kernel order)
-    _Float16 *W, *Ut, *M, *QG, *KLt;
+    _Float16 *W, *Tb, *M, *QG, *KLt;   // Tb: T diag(beta)
     float *GL;
     int slots;
 };
@@ -226,9 +204,8 @@ template <int DK, int DV> struct IntraMain {
         float scr[9][16][20];                 // inversion scratch (16x16 fp32 blocks)
     } r1;
     _Float16 KGt[DK][C + PADH];               // (beta K exp(G))^T
-    union {
+    struct {
         float A[C][C + 1];                    // beta-scaled strictly-lower A
-        _Float16 Vt[DV][C];                   // (beta V)^T, 16 B chunks XOR-swizzled by row
     } r3;
     float T[C][C + 1];                        // M during the levels, then T = (I + A)^-1
 };
@@ -240,12 +217,6 @@ template <int DK, int DV> struct IntraSmem {
     } u;
 };
 
-// Column of token t in row j of Vt: the 16-byte group is XORed with
-// (j ^ j/8) mod 8.  The MFMA B-operand reads (8 consecutive rows j, one group
-// each) and the transposing writes (a wave holds 16 channel groups of 8 and
-// 4 tokens, one channel offset j mod 8 per instruction) then spread over the
-// banks.
-__device__ __forceinline__ int vt_col(int j, int t) { return t ^ (((j ^ (j >> 3)) & 7) << 3); }
 
 // Gate threads: thread = (channel pair cp: channels 2cp, 2cp+1; eighth e8:
 // tokens t = 8 e8 + tau, tau = 0..7).  Token bit LVL says whether t is a row
@@ -424,15 +395,12 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 
     const IO *qg = reinterpret_cast<const IO *>(a.q);
     const IO *kg = reinterpret_cast<const IO *>(a.k);
-    const IO *vg = reinterpret_cast<const IO *>(a.v);
 
-    // ---- phase 0: every input load issued at once; V stays in registers ----
+    // ---- phase 0: every input load issued at once ----
     // Gate threads (channel pair cp: channels 2cp, 2cp+1; eighth e8: tokens
     // 8 e8 .. 8 e8 + 7) load their k, q and g values straight into registers:
     // one wave-wide load covers a whole token row.  With K = 128 the eighth is
-    // the wave.  The V tile is loaded by all threads with 16-byte loads.
-    constexpr int KV = 16 / sizeof(IO);                       // io elements per 16-byte load
-    constexpr int UV = C * DV / KV, NV = (UV + NTI - 1) / NTI;
+    // the wave.  (v is read by the state kernel only.)
     // Chunk bases are uniform; per-lane byte offsets stay below 64 rows of one
     // token stride (< 2^32 for any grid the launch accepts).
     const char *kb = reinterpret_cast<const char *>(kg + ((size_t)t0 * a.hk + hk) * DK);
@@ -442,10 +410,9 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     using GE = typename std::conditional<RAW, IO, float>::type;   // stored gate / beta element
     const char *gb = reinterpret_cast<const char *>(RAW ? a.gx : static_cast<const void *>(a.g)) +
                      ((size_t)t0 * a.hv + h) * (SCALAR ? 1 : DK) * sizeof(GE);
-    const char *vb = reinterpret_cast<const char *>(vg + ((size_t)t0 * a.hv + h) * DV);
     const GE *bb = reinterpret_cast<const GE *>(RAW ? a.bx : static_cast<const void *>(a.beta)) +
                    (size_t)t0 * a.hv + h;
-    const unsigned kq_row = (unsigned)a.hk * DK * sizeof(IO), v_row = (unsigned)a.hv * DV * sizeof(IO);
+    const unsigned kq_row = (unsigned)a.hk * DK * sizeof(IO);
     const unsigned g_row = (unsigned)a.hv * (SCALAR ? 1 : DK) * sizeof(GE);
     const bool fthread = tid < 4 * DK;
     const int cp = tid % (DK / 2), e8 = DK == 128 ? wave : tid / (DK / 2);
@@ -454,7 +421,6 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     using GRaw = typename std::conditional<SCALAR, GE, GPair>::type;
     Pair kraw[8], qraw[8];
     GRaw graw[8];
-    u32x4 vraw[NV];
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
         const int r = 8 * e8 + tau;
@@ -484,12 +450,6 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
                 dtb = f32x2{db[0] * kLog2e, db[1] * kLog2e};
             }
         }
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = tid + i * NTI, r = e / (DV / KV), c0 = (e % (DV / KV)) * KV;
-        vraw[i] = u32x4{0u, 0u, 0u, 0u};
-        if (e < UV && r < L) vraw[i] = *reinterpret_cast<const u32x4 *>(vb + (unsigned)r * v_row + (unsigned)c0 * sizeof(IO));
     }
     // A: the diagonal blocks' diagonal and upper triangle are zero (while the loads are in flight)
     for (int e = tid; e < 4 * 256; e += NTI) {
@@ -725,37 +685,20 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         __syncthreads();
     }
 
-    // ---- (beta V)^T into the (now free) A region ----
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = tid + i * NTI, r = e / (DV / KV), c0 = (e % (DV / KV)) * KV;
-        if (e < UV) {
-            const float b = sm.beta[r];
-#pragma unroll
-            for (int u = 0; u < KV; ++u) {
-                float x;
-                if constexpr (KV == 8) x = __uint_as_float(u & 1 ? (vraw[i][u >> 1] & 0xffff0000u) : (vraw[i][u >> 1] << 16));
-                else x = __uint_as_float(vraw[i][u]);
-                const int j = c0 + u;
-                sm.u.m.r3.Vt[j][vt_col(j, r)] = (_Float16)(b * x);
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- W = T (beta K exp(G)) -> LDS stage -> global tiles;  Ut = T (beta V) -> global acc tiles ----
+    // ---- W = T (beta K exp(G)) -> LDS stage -> global tiles (waves 0..3);
+    //      T diag(beta) -> global A-operand tiles (waves 4..7) ----
     {
         const int m = lane & 15, kq = lane >> 4;
         const int rt = wave & 3, which = wave >> 2;
-        f16x8 ta[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const float *tp = &sm.u.m.T[16 * rt + m][kk * 32 + kq * 8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ta[kk][e] = (_Float16)tp[e];
-        }
         const bool k1 = rt >= 2;   // T rows < 32 vanish for columns >= 32
         if (which == 0) {
+            f16x8 ta[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const float *tp = &sm.u.m.T[16 * rt + m][kk * 32 + kq * 8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ta[kk][e] = (_Float16)tp[e];
+            }
 #pragma unroll
             for (int ct = 0; ct < DK / 16; ++ct) {
                 f32x4 acc = mfma_f16(ta[0], lds8(&sm.u.m.KGt[16 * ct + m][kq * 8]), zero4());
@@ -772,16 +715,20 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
                 *reinterpret_cast<f16x8 *>(Wg + ((size_t)kk * 64 + lane) * 8) =
                     lds8(&sm.u.m.r1.stage[16 * rt + m][32 * kk + 8 * kq]);
         } else {
-            _Float16 *Ug = w.Ut + sh * C * DV;
+            // Ut = T diag(beta) V is formed by the state kernel from the v rows
+            // it streams; T diag(beta) goes out as A-operand tiles (rt, kk),
+            // the zero tile (rt < 2, kk = 1) not stored.
+            _Float16 *Tg = w.Tb + sh * C * C + (size_t)rt * 2 * 512;
 #pragma unroll
-            for (int ct = 0; ct < DV / 16; ++ct) {
-                const int j = 16 * ct + m;
-                f32x4 acc = mfma_f16(ta[0], lds8(&sm.u.m.r3.Vt[j][vt_col(j, kq * 8)]), zero4());
-                if (k1) acc = mfma_f16(ta[1], lds8(&sm.u.m.r3.Vt[j][vt_col(j, 32 + kq * 8)]), acc);
-                f16x4 h4;
+            for (int kk = 0; kk < 2; ++kk) {
+                if (kk == 0 || k1) {
+                    const float *tp = &sm.u.m.T[16 * rt + m][kk * 32 + kq * 8];
+                    const float *bp = &sm.beta[kk * 32 + kq * 8];
+                    f16x8 tb;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) h4[jj] = (_Float16)acc[jj];
-                *reinterpret_cast<f16x4 *>(Ug + ((size_t)(rt * (DV / 16) + ct) * 64 + lane) * 4) = h4;
+                    for (int e = 0; e < 8; ++e) tb[e] = (_Float16)(tp[e] * bp[e]);
+                    *reinterpret_cast<f16x8 *>(Tg + ((size_t)kk * 64 + lane) * 8) = tb;
+                }
             }
         }
     }
@@ -800,10 +747,13 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 // One workgroup of eight waves owns one (sequence, head) chain and the whole
 // K x V state.  Per chunk:
 //   (a) every wave writes its state tiles to LDS as fp16 (S^T, B operand);
-//   (b) waves 0..3 (token row tile rt = wave): U = Ut - W S  -> LDS (U^T);
+//   (b) waves 0..3 (token row tile rt = wave): U = Ut - W S -> LDS (U^T),
+//       where Ut = (T diag(beta)) V was formed at the end of the previous
+//       step from V^T staged in LDS (v is streamed once, by this kernel only);
 //       waves 4..7 (rt = wave - 4): the inter-chunk output part Q exp(G) S;
 //   (c) waves 4..7: O = scale (Q exp(G) S + M U), staged, stored as rows;
-//   (d) every wave: its state tiles S <- exp(G_last) S + (K exp(G_last - G))^T U.
+//   (d) every wave: its state tiles S <- exp(G_last) S + (K exp(G_last - G))^T U;
+//       waves 0..3 then form the next chunk's Ut (off the chain's critical path).
 // Each operand register is reloaded with the next chunk's tile right after
 // its last use, so its load has a whole chunk step to arrive with a single
 // register copy; the register budget then admits two workgroups per CU and
@@ -815,6 +765,7 @@ constexpr int NTS = 512;   // threads of the state kernel
 template <int DK, int DV, typename IO> struct StateSmem {
     _Float16 Sh[DV][DK + PADH];   // S^T as fp16 (B operand of W S and Q exp(G) S)
     _Float16 Vn[DV][C + PADH];    // U^T as fp16 (B operand of M U and KLt U)
+    _Float16 Vs[2][DV][C + PADH]; // V^T of a chunk as fp16 (B operand of (T diag(beta)) V), two buffers
     IO Ost[4][16][DV + 16 / sizeof(IO)];   // output rows of waves 4..7, for 16-byte stores
 };
 
@@ -831,8 +782,6 @@ __device__ __forceinline__ void store_state4(bf16 *p, const f32x4 &v) {
     *reinterpret_cast<u32x2 *>(p) = w;
 }
 
-__device__ __forceinline__ f16x8 gld8(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
-__device__ __forceinline__ f16x4 gld4(const _Float16 *p) { return *reinterpret_cast<const f16x4 *>(p); }
 
 // Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
 // no swizzle; untyped 16-byte accesses with a byte range check.
@@ -858,7 +807,6 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
     // workgroups by columns); memory strides use the full width DV.
     constexpr int KK = DK / 32;               // k-steps over key channels
     constexpr int CT = DVW / 16;              // value column tiles of this workgroup
-    constexpr int CTF = DV / 16;              // value column tiles of the full state
     constexpr int R = DK / 16;                // key row tiles of the state
     constexpr int NST = R * CT;               // state tiles
     constexpr int NTW = NST >= 8 ? NST / 8 : 1;   // state tiles per wave (one key row tile)
@@ -896,11 +844,12 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
     // the next chunk's tiles right after their last use).  Chunk bases are
     // wave-uniform (see uniform_off); each lane adds a 32-bit byte offset.
     f16x8 Xa[KK];                   // W (U waves) or Q exp(G) (output waves), row tile rt
-    f16x4 Ua[UW ? CT : 1];          // Ut of row tile rt (U waves)
+    f16x8 Ta[UW ? 2 : 1];           // T diag(beta) of row tile rt (U waves)
     f16x8 Ma[UW ? 1 : 2];           // M of row tile rt (output waves)
     f16x8 Ka[2];                    // (K exp(G_last - G))^T, key row tile kr
     f32x4 gl;                       // exp(G_last) of key rows 16 kr + 4 kq + jj
     auto chunk_base = [&](int ch) { return (size_t)(s0 + ch) * a.hv + h; };
+    const bool t_hi = rt >= 2;      // token row tile rt reaches columns 32..63 of T and M
     const unsigned lane16 = (unsigned)lane * 16u;
     // The lane offset is re-derived behind an empty asm at every use, so the
     // compiler cannot pre-add it to loop-invariant 64-bit per-lane pointers.
@@ -912,25 +861,25 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
     auto ld8 = [](const _Float16 *base, unsigned off) {
         return *reinterpret_cast<const f16x8 *>(reinterpret_cast<const char *>(base) + off);
     };
-    auto ld4 = [](const _Float16 *base, unsigned off) {
-        return *reinterpret_cast<const f16x4 *>(reinterpret_cast<const char *>(base) + off);
-    };
     auto load_x = [&](int ch) {
         const size_t sh = chunk_base(ch);
         const _Float16 *Xg = (UW ? w.W : w.QG) + uniform_off(sh * C * DK + (size_t)rt * KK * 512);
         const unsigned lo16 = lane_off(16u);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) Xa[kk] = ld8(Xg, lo16 + kk * 1024u);
+    };
+    // T diag(beta) of row tile rt (U waves): its tile of columns 32..63 is zero for rt < 2
+    [[maybe_unused]] auto load_t = [&](int ch) {
         if constexpr (UW) {
-            const _Float16 *Ug = w.Ut + uniform_off(sh * C * DV + ((size_t)rt * CTF + j0 / 16) * 256);
-            const unsigned lo8 = lane_off(8u);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) Ua[ct] = ld4(Ug, lo8 + ct * 512u);
+            const _Float16 *Tg = w.Tb + uniform_off(chunk_base(ch) * C * C + (size_t)rt * 2 * 512);
+            const unsigned lo16 = lane_off(16u);
+            Ta[0] = ld8(Tg, lo16);
+            Ta[1] = t_hi ? ld8(Tg, lo16 + 1024u) : f16x8{};
         }
     };
     // M is lower triangular: the tile of token rows 16 rt.. and columns 32..63
     // is zero (and not stored) for rt < 2.
-    const bool m_hi = rt >= 2;
+    const bool m_hi = t_hi;
     auto load_m = [&](int ch) {
         if constexpr (!UW) {
             const _Float16 *Mg = w.M + uniform_off(chunk_base(ch) * C * C + (size_t)rt * 2 * 512);
@@ -950,10 +899,81 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
         asm volatile("" : "+v"(go));
         gl = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const char *>(Gg) + go);
     };
+    // V staging (U waves): unit u = (token pair p = u % 32, column group
+    // g = u / 32) moves 16 bytes (VPT columns) of token rows 2p and 2p + 1 of
+    // this part's columns.  The loads go through a buffer whose range is the
+    // chunk's valid rows, so rows past the sequence end read as zero.
+    constexpr int VPT = 16 / (int)sizeof(IO);   // io columns per 16-byte load
+    constexpr int NVU = 32 * (DVW / VPT);       // units
+    constexpr int NVI = (NVU + 255) / 256;      // units per U-wave thread
+    static_assert(NVU % 64 == 0, "V staging units cover whole waves");
+    [[maybe_unused]] u32x4 Vr[UW ? NVI : 1][2];
+    const int vrow = a.hv * DV * (int)sizeof(IO);   // token stride of v, bytes
+    [[maybe_unused]] auto load_v = [&](int ch) {
+        if constexpr (UW) {
+            const int t0c = tbeg + ch * C, Lc = min(C, tend - t0c);
+            char *vb = reinterpret_cast<char *>(const_cast<void *>(a.v)) +
+                       uniform_off((((size_t)t0c * a.hv + h) * DV + j0) * sizeof(IO));
+            const int nrec = __builtin_amdgcn_readfirstlane(Lc > 0 ? (Lc - 1) * vrow + DVW * (int)sizeof(IO) : 0);
+            const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(vb, 0, nrec, kBufferWord3);
+#pragma unroll
+            for (int it = 0; it < NVI; ++it) {
+                const int u = wave * 64 + lane + 256 * it;
+                if (u < NVU) {   // wave-uniform
+                    const int off = 2 * (u % 32) * vrow + (u / 32) * 16;
+                    Vr[it][0] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
+                    Vr[it][1] = __builtin_amdgcn_raw_buffer_load_b128(vr, off + vrow, 0, 0);
+                }
+            }
+        }
+    };
+    [[maybe_unused]] auto write_vs = [&](int buf) {
+        if constexpr (UW) {
+#pragma unroll
+            for (int it = 0; it < NVI; ++it) {
+                const int u = wave * 64 + lane + 256 * it;
+                if (u < NVU) {
+                    const int p = u % 32, g = u / 32;
+#pragma unroll
+                    for (int e = 0; e < VPT; ++e) {
+                        float x0, x1;
+                        if constexpr (VPT == 8) {
+                            x0 = __uint_as_float(e & 1 ? (Vr[it][0][e >> 1] & 0xffff0000u) : (Vr[it][0][e >> 1] << 16));
+                            x1 = __uint_as_float(e & 1 ? (Vr[it][1][e >> 1] & 0xffff0000u) : (Vr[it][1][e >> 1] << 16));
+                        } else {
+                            x0 = __uint_as_float(Vr[it][0][e]);
+                            x1 = __uint_as_float(Vr[it][1][e]);
+                        }
+                        *reinterpret_cast<f16x2 *>(&sm.Vs[buf][g * VPT + e][2 * p]) = f16x2{(_Float16)x0, (_Float16)x1};
+                    }
+                }
+            }
+        }
+    };
+
+    // Ut = (T diag(beta)) V of row tile rt for the chunk whose V^T is in buffer buf (U waves)
+    [[maybe_unused]] f32x4 Ut[UW ? CT : 1];
+    [[maybe_unused]] auto form_ut = [&](int buf) {
+        if constexpr (UW) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                Ut[ct] = mfma_f16(Ta[0], lds8(&sm.Vs[buf][16 * ct + m][kq * 8]), zero4());
+                if (t_hi) Ut[ct] = mfma_f16(Ta[1], lds8(&sm.Vs[buf][16 * ct + m][32 + kq * 8]), Ut[ct]);
+            }
+        }
+    };
+
     if (nchunks > 0) {
         load_x(0);
         load_m(0);
         if (swave) load_k(0);
+        load_t(0);
+        load_v(0);
+        write_vs(0);                        // V^T of chunk 0
+        load_v(min(1, nchunks - 1));
+        __syncthreads();
+        form_ut(0);
+        load_t(min(1, nchunks - 1));
     }
 
     IO *og = reinterpret_cast<IO *>(a.o);
@@ -964,6 +984,13 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
         // the number of memory operations between a load and its use is the
         // same on every path and the waits stay exact.
         const int nxt = min(ch + 1, nchunks - 1);
+
+        // V^T of the next chunk into the other buffer (its previous chunk was
+        // read before this step's first barrier), the chunk after it into registers
+        if constexpr (UW) {
+            write_vs((ch + 1) & 1);
+            load_v(min(ch + 2, nchunks - 1));
+        }
 
         // (a) S^T -> fp16 LDS
         if (swave) {
@@ -977,7 +1004,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
         }
         __syncthreads();
 
-        // (b) U = Ut - W S (U waves) | Q exp(G) S (output waves), row tile rt
+        // (b) U = (T diag(beta)) V - W S (U waves) | Q exp(G) S (output waves), row tile rt
         [[maybe_unused]] f32x4 Oacc[UW ? 1 : CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -988,7 +1015,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             if constexpr (UW) {
                 f16x4 uv;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) uv[jj] = (_Float16)((float)Ua[ct][jj] - acc[jj]);
+                for (int jj = 0; jj < 4; ++jj) uv[jj] = (_Float16)(Ut[ct][jj] - acc[jj]);
                 *reinterpret_cast<f16x4 *>(&sm.Vn[16 * ct + m][16 * rt + 4 * kq]) = uv;
             } else {
                 Oacc[ct] = acc;
@@ -1043,6 +1070,13 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             }
             load_k(nxt);
         }
+        // the next chunk's Ut (its V^T was written before this step's first
+        // barrier, its T diag(beta) tiles loaded a step ago), then the tiles
+        // of the chunk after it
+        if constexpr (UW) {
+            form_ut((ch + 1) & 1);
+            load_t(min(ch + 2, nchunks - 1));
+        }
     }
 
     if (row_out >= 0 && swave) {
@@ -1087,7 +1121,8 @@ hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
     dim3 grid((unsigned)((items + kXcd - 1) / kXcd * kXcd));
     auto kern = a.raw_gate ? (a.scalar_gate ? intra_kernel<DK, DV, IO, true, true> : intra_kernel<DK, DV, IO, false, true>)
                            : (a.scalar_gate ? intra_kernel<DK, DV, IO, true, false> : intra_kernel<DK, DV, IO, false, false>);
-    hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
     kern<<<grid, NTI, smem, s>>>(a, w);
     return hipGetLastError();
 }
@@ -1097,7 +1132,8 @@ hipError_t launch_state_w(PrefillArgs &a, Work &w, hipStream_t s) {
     // 1-D grid over (sequence rank, head) chains, rank-major, times the column parts
     const size_t smem = sizeof(StateSmem<DK, DVW, IO>);
     auto kern = state_kernel<DK, DV, DVW, IO, ST>;
-    hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
     const long chains = (long)a.hv * a.num_seqs;
     const long blocks = DV == DVW ? chains : (chains + kXcd - 1) / kXcd * kXcd * (DV / DVW);
     kern<<<dim3((unsigned)blocks), NTS, smem, s>>>(a, w);
@@ -1106,13 +1142,12 @@ hipError_t launch_state_w(PrefillArgs &a, Work &w, hipStream_t s) {
 
 template <int DK, int DV, typename IO, typename ST>
 hipError_t launch_state_st(PrefillArgs &a, Work &w, hipStream_t s) {
-    // Split a chain's 128 value columns over two workgroups while the chains
-    // alone do not fill the device twice over: the per-chunk critical path of
-    // a chain halves, and the longest chains set the kernel's end.
-    if constexpr (DV == 128) {
-        if (state_split(a.hv, a.num_seqs, DV) > 1) return launch_state_w<DK, DV, DV / 2, IO, ST>(a, w, s);
-    }
-    return launch_state_w<DK, DV, DV, IO, ST>(a, w, s);
+    // A chain's 128 value columns are split over two workgroups: the
+    // per-chunk critical path of a chain halves (the longest chains set the
+    // kernel's end), and the V^T staging block stays at 64 columns.
+    constexpr int DVW = DV == 128 ? 64 : DV;
+    static_assert(DV / DVW == (DV == 128 ? 2 : 1), "column parts");
+    return launch_state_w<DK, DV, DVW, IO, ST>(a, w, s);
 }
 
 template <int DK, int DV, typename IO>
@@ -1158,7 +1193,7 @@ hipError_t launch_prefill(PrefillArgs &a, void *workspace, hipStream_t stream) {
     w.chunk_off = reinterpret_cast<int32_t *>(base + l.chunk_off);
     w.seq_order = reinterpret_cast<int32_t *>(base + l.seq_order);
     w.W = reinterpret_cast<_Float16 *>(base + l.W);
-    w.Ut = reinterpret_cast<_Float16 *>(base + l.Ut);
+    w.Tb = reinterpret_cast<_Float16 *>(base + l.Tb);
     w.M = reinterpret_cast<_Float16 *>(base + l.M);
     w.QG = reinterpret_cast<_Float16 *>(base + l.QG);
     w.KLt = reinterpret_cast<_Float16 *>(base + l.KLt);

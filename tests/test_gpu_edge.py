@@ -8,8 +8,8 @@ against the fp64 oracle through the C ABI:
 * wide GQA (one key head for eight value heads);
 * many short sequences, including more than the meta kernel ranks by length
   (the natural order is kept beyond that count) and more than one scan block;
-* 128 value columns with more (sequence, head) chains than the state kernel
-  splits by columns, so the unsplit path runs too.
+* 1200 (sequence, head) chains with 128 value columns (2400 column parts of
+  the state kernel), many of them empty.
 """
 import numpy as np
 import pytest
@@ -77,10 +77,10 @@ def test_many_short_sequences(K, oracle, n):
     run_and_check(K, oracle, inp, "N=%d short" % n)
 
 
-def test_unsplit_state_chains(K, oracle):
-    """600 sequences x 2 heads = 1200 chains with V = 128: above the count for
-    which the state kernel splits each chain's value columns over two
-    workgroups, so every chain runs whole in one workgroup."""
+def test_many_state_chains(K, oracle):
+    """600 sequences (lengths 0..79) x 2 heads = 1200 chains with V = 128,
+    each split over two column parts: 2400 state workgroups, more than are
+    resident at once, with empty and one-chunk chains among them."""
     g = torch.Generator().manual_seed(76)
     lens = torch.randint(0, 80, (600,), generator=g).tolist()
     inp = W.make_prefill(76, lens, 1, 2, 128, 128, gate="realistic", h0="random")
