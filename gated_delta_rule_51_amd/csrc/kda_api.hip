@@ -110,8 +110,7 @@ kda_status prefill_impl(const kda_prefill_desc *d, const void *q, const void *k,
         return KDA_ERR_HIP;
     const long slots = (T + 63L * N) / 64;
     const long intra_wgs = (slots * d->hv + 7) / 8 * 8;
-    const long chains = (long)d->hv * N, split = kda::state_split(d->dv);
-    const long state_wgs = split > 1 ? (chains + 7) / 8 * 8 * split : chains;
+    const long state_wgs = (long)d->hv * N;   // one workgroup per (sequence, head) chain
     if (intra_wgs > max_x || state_wgs > max_x) return KDA_ERR_UNSUPPORTED;
 
     kda::PrefillArgs a{};

@@ -51,9 +51,6 @@ struct PrefillArgs {
     bool io_bf16, state_bf16, scalar_gate, raw_gate;
 };
 
-// Column parts per (sequence, head) chain of the state kernel: 2 for 128
-// value columns, else 1.
-inline int state_split(int dv) { return dv == 128 ? 2 : 1; }
 
 size_t prefill_workspace_bytes(int num_seqs, int total_tokens, int hv, int dk, int dv);
 hipError_t launch_prefill(PrefillArgs &a, void *workspace, hipStream_t stream);

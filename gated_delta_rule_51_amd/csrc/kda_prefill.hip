@@ -744,8 +744,9 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 //     X[16 rt + 4 (l / 16) + jj][16 ct + l % 16], jj = 0..3  (8 B per lane)
 // so every operand load is one contiguous 16 B (or 8 B) access per lane.
 //
-// One workgroup of eight waves owns one (sequence, head) chain and the whole
-// K x V state.  Per chunk:
+// Eight waves own one column part (all of V <= 64, or 64 of 128 value
+// columns) of one (sequence, head) chain and that part of the K x V state;
+// a chain's parts share one workgroup.  Per chunk:
 //   (a) every wave writes its state tiles to LDS as fp16 (S^T, B operand);
 //   (b) waves 0..3 (token row tile rt = wave): U = Ut - W S -> LDS (U^T),
 //       where Ut = (T diag(beta)) V was formed at the end of the previous
@@ -756,11 +757,10 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 //       waves 0..3 then form the next chunk's Ut (off the chain's critical path).
 // Each operand register is reloaded with the next chunk's tile right after
 // its last use, so its load has a whole chunk step to arrive with a single
-// register copy; the register budget then admits two workgroups per CU and
-// every chain of a batch of up to 2 x CUs (sequence, head) pairs is resident
-// from the start.
+// register copy; the register budget (<= 128 VGPRs) then admits sixteen
+// waves per CU: one chain of 128 value columns, or two of at most 64.
 // ---------------------------------------------------------------------------
-constexpr int NTS = 512;   // threads of the state kernel
+constexpr int NTS = 512;   // threads of the state kernel per column part
 
 template <int DK, int DV, typename IO> struct StateSmem {
     _Float16 Sh[DV][DK + PADH];   // S^T as fp16 (B operand of W S and Q exp(G) S)
@@ -899,10 +899,11 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
         asm volatile("" : "+v"(go));
         gl = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const char *>(Gg) + go);
     };
-    // V staging (U waves): unit u = (token pair p = u % 32, column group
-    // g = u / 32) moves 16 bytes (VPT columns) of token rows 2p and 2p + 1 of
-    // this part's columns.  The loads go through a buffer whose range is the
-    // chunk's valid rows, so rows past the sequence end read as zero.
+    // V staging (U waves): unit u = (token pair p, column group g), with g
+    // fastest, moves 16 bytes (VPT columns) of token rows 2p and 2p + 1 of
+    // this part's columns, so a wave's loads cover whole row segments.  The
+    // loads go through a buffer whose range is the chunk's valid rows (rows
+    // past the sequence end read as zero) and are nontemporal: v is read once.
     constexpr int VPT = 16 / (int)sizeof(IO);   // io columns per 16-byte load
     constexpr int NVU = 32 * (DVW / VPT);       // units
     constexpr int NVI = (NVU + 255) / 256;      // units per U-wave thread
@@ -920,9 +921,9 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             for (int it = 0; it < NVI; ++it) {
                 const int u = wave * 64 + lane + 256 * it;
                 if (u < NVU) {   // wave-uniform
-                    const int off = 2 * (u % 32) * vrow + (u / 32) * 16;
-                    Vr[it][0] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
-                    Vr[it][1] = __builtin_amdgcn_raw_buffer_load_b128(vr, off + vrow, 0, 0);
+                    const int off = 2 * (u / (NVU / 32)) * vrow + (u % (NVU / 32)) * 16;
+                    Vr[it][0] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 2);
+                    Vr[it][1] = __builtin_amdgcn_raw_buffer_load_b128(vr, off + vrow, 0, 2);
                 }
             }
         }
@@ -933,7 +934,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             for (int it = 0; it < NVI; ++it) {
                 const int u = wave * 64 + lane + 256 * it;
                 if (u < NVU) {
-                    const int p = u % 32, g = u / 32;
+                    const int p = u / (NVU / 32), g = u % (NVU / 32);
 #pragma unroll
                     for (int e = 0; e < VPT; ++e) {
                         float x0, x1;
@@ -1087,26 +1088,24 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
     }
 }
 
+// One workgroup per (sequence, head) chain.  With DV / DVW column parts it
+// has eight waves per part; the parts keep their own LDS blocks and share
+// only the barriers, so they step through the chunks in lockstep and the
+// operand tiles both parts load (W, Q exp(G), M, the key factors, T diag(beta))
+// are fetched from HBM once and served to the second part by the caches.
 template <int DK, int DV, int DVW, typename IO, typename ST>
-__global__ __launch_bounds__(NTS, 4) void state_kernel(PrefillArgs a, Work w) {
+__global__ __launch_bounds__(NTS * (DV / DVW)) void state_kernel(PrefillArgs a, Work w) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    StateSmem<DK, DVW, IO> &sm = *reinterpret_cast<StateSmem<DK, DVW, IO> *>(smem_raw);
-    // (sequence rank, head) chains, rank-major: the longest sequences come
-    // first.  With NSPLIT > 1 the NSPLIT column parts of a chain get block ids
-    // kXcd apart inside one group of kXcd chains: the ids go round robin over
-    // the XCDs, so the parts share one XCD (and its L2) and start together.
-    constexpr int NSPLIT = DV / DVW;
-    int chain = blockIdx.x, part = 0;
-    if constexpr (NSPLIT > 1) {
-        const int grp = blockIdx.x / (kXcd * NSPLIT), r = blockIdx.x % (kXcd * NSPLIT);
-        part = r / kXcd;
-        chain = grp * kXcd + r % kXcd;
-    }
+    StateSmem<DK, DVW, IO> *parts = reinterpret_cast<StateSmem<DK, DVW, IO> *>(smem_raw);
+    // (sequence rank, head) chains, rank-major: the longest sequences come first
+    const int chain = blockIdx.x;
     const int h = chain % a.hv, rank = chain / a.hv;
     if (rank >= a.num_seqs) return;
     const int n = w.seq_order[rank];
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int part = wv / 8, wave = wv % 8;
+    StateSmem<DK, DVW, IO> &sm = parts[part];
     if (wave < 4) state_chain<true, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);    // U waves
     else state_chain<false, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);   // output waves
 }
@@ -1129,22 +1128,23 @@ hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
 
 template <int DK, int DV, int DVW, typename IO, typename ST>
 hipError_t launch_state_w(PrefillArgs &a, Work &w, hipStream_t s) {
-    // 1-D grid over (sequence rank, head) chains, rank-major, times the column parts
-    const size_t smem = sizeof(StateSmem<DK, DVW, IO>);
+    // 1-D grid over (sequence rank, head) chains, rank-major; eight waves per column part
+    constexpr int NPART = DV / DVW;
+    const size_t smem = NPART * sizeof(StateSmem<DK, DVW, IO>);
     auto kern = state_kernel<DK, DV, DVW, IO, ST>;
     const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     const long chains = (long)a.hv * a.num_seqs;
-    const long blocks = DV == DVW ? chains : (chains + kXcd - 1) / kXcd * kXcd * (DV / DVW);
-    kern<<<dim3((unsigned)blocks), NTS, smem, s>>>(a, w);
+    kern<<<dim3((unsigned)chains), NTS * NPART, smem, s>>>(a, w);
     return hipGetLastError();
 }
 
 template <int DK, int DV, typename IO, typename ST>
 hipError_t launch_state_st(PrefillArgs &a, Work &w, hipStream_t s) {
-    // A chain's 128 value columns are split over two workgroups: the
-    // per-chunk critical path of a chain halves (the longest chains set the
-    // kernel's end), and the V^T staging block stays at 64 columns.
+    // A chain's 128 value columns are split over two column parts of one
+    // workgroup: the per-chunk critical path of a chain halves (the longest
+    // chains set the kernel's end), and each part's LDS blocks stay at 64
+    // value columns.
     constexpr int DVW = DV == 128 ? 64 : DV;
     static_assert(DV / DVW == (DV == 128 ? 2 : 1), "column parts");
     return launch_state_w<DK, DV, DVW, IO, ST>(a, w, s);
