@@ -586,18 +586,20 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         for (int u = 0; u < 2; ++u) {
             const int c = 2 * cp + u;
             const int ln = (c & 15) + 16 * (e8 & 3);
-            *reinterpret_cast<f16x8 *>(w.KLt + kl_off + ((size_t)((c >> 4) * 2 + (e8 >> 2)) * 64 + ln) * 8) =
-                u ? kl1 : kl0;
+            __builtin_nontemporal_store(u ? kl1 : kl0,
+                reinterpret_cast<f16x8 *>(w.KLt + kl_off + ((size_t)((c >> 4) * 2 + (e8 >> 2)) * 64 + ln) * 8));
         }
     }
     __syncthreads();
 
     // ---- A-operand tile stores: Q exp(G) and M (lower triangle incl. diagonal) ----
+    // (every workspace operand is written nontemporally: it is read back only
+    // by the state kernel, after this kernel, so it need not stay in the caches)
     for (int e = tid; e < (C / 16) * (DK / 32) * 64; e += NTI) {
         const int tile = e >> 6, l = e & 63;
         const int rt = tile / (DK / 32), kk = tile % (DK / 32);
-        *reinterpret_cast<f16x8 *>(w.QG + qg_off + (size_t)e * 8) =
-            lds8(&sm.u.m.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]);
+        __builtin_nontemporal_store(lds8(&sm.u.m.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]),
+            reinterpret_cast<f16x8 *>(w.QG + qg_off + (size_t)e * 8));
     }
     for (int e = tid; e < (C / 16) * (C / 32) * 64; e += NTI) {
         const int tile = e >> 6, l = e & 63;
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
             v[u] = (_Float16)(i0 + u < r ? sm.u.m.T[r][i0 + u] : i0 + u == r ? sm.mdiag[r] : 0.f);
-        *reinterpret_cast<f16x8 *>(w.M + sh * C * C + (size_t)e * 8) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<f16x8 *>(w.M + sh * C * C + (size_t)e * 8));
     }
     __syncthreads();
     // the blocks of T above the block diagonal are zero
@@ -712,8 +714,8 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
             _Float16 *Wg = w.W + sh * C * DK + (size_t)rt * (DK / 32) * 512;
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk)
-                *reinterpret_cast<f16x8 *>(Wg + ((size_t)kk * 64 + lane) * 8) =
-                    lds8(&sm.u.m.r1.stage[16 * rt + m][32 * kk + 8 * kq]);
+                __builtin_nontemporal_store(lds8(&sm.u.m.r1.stage[16 * rt + m][32 * kk + 8 * kq]),
+                    reinterpret_cast<f16x8 *>(Wg + ((size_t)kk * 64 + lane) * 8));
         } else {
             // Ut = T diag(beta) V is formed by the state kernel from the v rows
             // it streams; T diag(beta) goes out as A-operand tiles (rt, kk),
@@ -727,7 +729,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
                     f16x8 tb;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) tb[e] = (_Float16)(tp[e] * bp[e]);
-                    *reinterpret_cast<f16x8 *>(Tg + ((size_t)kk * 64 + lane) * 8) = tb;
+                    __builtin_nontemporal_store(tb, reinterpret_cast<f16x8 *>(Tg + ((size_t)kk * 64 + lane) * 8));
                 }
             }
         }
