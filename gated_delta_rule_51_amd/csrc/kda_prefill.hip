@@ -428,8 +428,8 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         graw[tau] = GRaw{};
         if (fthread && r < L) {
             const unsigned off = (unsigned)r * kq_row + (unsigned)cp * 2 * sizeof(IO);
-            kraw[tau] = *reinterpret_cast<const Pair *>(kb + off);
-            qraw[tau] = *reinterpret_cast<const Pair *>(qb + off);
+            kraw[tau] = __builtin_nontemporal_load(reinterpret_cast<const Pair *>(kb + off));
+            qraw[tau] = __builtin_nontemporal_load(reinterpret_cast<const Pair *>(qb + off));
             graw[tau] = *reinterpret_cast<const GRaw *>(gb + (unsigned)r * g_row +
                                                         (SCALAR ? 0u : (unsigned)cp * 2 * sizeof(GE)));
         }
@@ -1056,7 +1056,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             for (int e = lane; e < 16 * VPR; e += 64) {
                 const int rr = e / VPR, c0 = (e % VPR) * EPV;
                 __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(&sm.Ost[ow][rr][c0]), orsrc,
-                                                       rr * orow + c0 * (int)sizeof(IO), 0, 0);
+                                                       rr * orow + c0 * (int)sizeof(IO), 0, 2);
             }
         }
 
