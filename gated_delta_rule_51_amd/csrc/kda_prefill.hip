@@ -793,6 +793,10 @@ constexpr int kBufferWord3 = 0x00020000;
 // readfirstlane).  Added to a kernel-argument pointer it keeps the global
 // address space, and the compiler cannot fold per-lane offsets into a
 // loop-invariant 64-bit per-lane pointer per operand stream.
+// Keeps the loads issued before it from being sunk past it by the compiler
+// (a prefetch sunk to its use would expose the full memory latency).
+__device__ __forceinline__ void pin_loads() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ size_t uniform_off(size_t x) {
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
     const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
@@ -876,7 +880,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             const _Float16 *Tg = w.Tb + uniform_off(chunk_base(ch) * C * C + (size_t)rt * 2 * 512);
             const unsigned lo16 = lane_off(16u);
             Ta[0] = ld8(Tg, lo16);
-            Ta[1] = t_hi ? ld8(Tg, lo16 + 1024u) : f16x8{};
+            Ta[1] = ld8(Tg, lo16 + 1024u);   // unused (and not stored) for rt < 2
         }
     };
     // M is lower triangular: the tile of token rows 16 rt.. and columns 32..63
@@ -887,7 +891,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             const _Float16 *Mg = w.M + uniform_off(chunk_base(ch) * C * C + (size_t)rt * 2 * 512);
             const unsigned lo16 = lane_off(16u);
             Ma[0] = ld8(Mg, lo16);
-            Ma[1] = m_hi ? ld8(Mg, lo16 + 1024u) : f16x8{};
+            Ma[1] = ld8(Mg, lo16 + 1024u);   // unused (and not stored) for rt < 2
         }
     };
     auto load_k = [&](int ch) {
@@ -922,7 +926,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
 #pragma unroll
             for (int it = 0; it < NVI; ++it) {
                 const int u = wave * 64 + lane + 256 * it;
-                if (u < NVU) {   // wave-uniform
+                if (NVU % 256 == 0 || u < NVU) {   // wave-uniform
                     const int off = 2 * (u / (NVU / 32)) * vrow + (u % (NVU / 32)) * 16;
                     Vr[it][0] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 2);
                     Vr[it][1] = __builtin_amdgcn_raw_buffer_load_b128(vr, off + vrow, 0, 2);
@@ -935,7 +939,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
 #pragma unroll
             for (int it = 0; it < NVI; ++it) {
                 const int u = wave * 64 + lane + 256 * it;
-                if (u < NVU) {
+                if (NVU % 256 == 0 || u < NVU) {
                     const int p = u / (NVU / 32), g = u % (NVU / 32);
 #pragma unroll
                     for (int e = 0; e < VPT; ++e) {
@@ -966,16 +970,21 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
         }
     };
 
+    // The prologue ends with the loads the loop issues between a chunk's V
+    // loads and the next loop head (x, k, t for U waves; x, m, k for output
+    // waves), in the same order and number, so the compiler's vector-memory
+    // waits at the loop head are exact on both incoming paths and the loads
+    // of the next chunk stay in flight.
     if (nchunks > 0) {
-        load_x(0);
-        load_m(0);
-        if (swave) load_k(0);
         load_t(0);
         load_v(0);
         write_vs(0);                        // V^T of chunk 0
-        load_v(min(1, nchunks - 1));
         __syncthreads();
         form_ut(0);
+        load_v(min(1, nchunks - 1));
+        load_x(0);
+        load_m(0);
+        if (swave) load_k(0);
         load_t(min(1, nchunks - 1));
     }
 
@@ -993,6 +1002,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
         if constexpr (UW) {
             write_vs((ch + 1) & 1);
             load_v(min(ch + 2, nchunks - 1));
+            pin_loads();
         }
 
         // (a) S^T -> fp16 LDS
@@ -1027,6 +1037,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             if (UW || (ct & 1)) __builtin_amdgcn_sched_barrier(0);
         }
         load_x(nxt);
+        pin_loads();
         __syncthreads();
 
         // (c) O = scale (Q exp(G) S + M U), output waves; valid rows stored
@@ -1042,6 +1053,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
                 if (ct & 1) __builtin_amdgcn_sched_barrier(0);
             }
             load_m(nxt);
+            pin_loads();
             wave_sync();
             // 16 rows x DV values of this wave -> 16-byte buffer stores.  The
             // buffer's range is the valid rows of this tile, so the stores of
@@ -1072,6 +1084,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
                 if (c & 1) __builtin_amdgcn_sched_barrier(0);
             }
             load_k(nxt);
+            pin_loads();
         }
         // the next chunk's Ut (its V^T was written before this step's first
         // barrier, its T diag(beta) tiles loaded a step ago), then the tiles
@@ -1079,6 +1092,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
         if constexpr (UW) {
             form_ut((ch + 1) & 1);
             load_t(min(ch + 2, nchunks - 1));
+            pin_loads();
         }
     }
 
