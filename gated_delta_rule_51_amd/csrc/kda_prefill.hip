@@ -592,51 +592,57 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     }
     __syncthreads();
 
-    // ---- A-operand tile stores: Q exp(G) and M (lower triangle incl. diagonal) ----
-    // (every workspace operand is written nontemporally: it is read back only
-    // by the state kernel, after this kernel, so it need not stay in the caches)
-    for (int e = tid; e < (C / 16) * (DK / 32) * 64; e += NTI) {
-        const int tile = e >> 6, l = e & 63;
-        const int rt = tile / (DK / 32), kk = tile % (DK / 32);
-        __builtin_nontemporal_store(lds8(&sm.u.m.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]),
-            reinterpret_cast<f16x8 *>(w.QG + qg_off + (size_t)e * 8));
-    }
-    for (int e = tid; e < (C / 16) * (C / 32) * 64; e += NTI) {
-        const int tile = e >> 6, l = e & 63;
-        if ((tile & 1) && (tile >> 1) < 2) continue;   // rows < 32, columns >= 32: zero, never read
-        const int r = 16 * (tile >> 1) + (l & 15), i0 = 32 * (tile & 1) + 8 * (l >> 4);
-        f16x8 v;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            v[u] = (_Float16)(i0 + u < r ? sm.u.m.T[r][i0 + u] : i0 + u == r ? sm.mdiag[r] : 0.f);
-        __builtin_nontemporal_store(v, reinterpret_cast<f16x8 *>(w.M + sh * C * C + (size_t)e * 8));
-    }
-    __syncthreads();
-    // the blocks of T above the block diagonal are zero
-    for (int e = tid; e < C * C; e += NTI) {
-        const int r = e / C, i = e % C;
-        if ((i >> 4) > (r >> 4)) sm.u.m.T[r][i] = 0.f;
-    }
-
-    // ---- T = (I + A)^-1: diagonal blocks by forward substitution (wave 0) ----
-    // Each lane owns one column c of one 16x16 diagonal block b and runs the
-    // unit lower triangular forward substitution in fp32:
+    // ---- wave 0: diagonal blocks of T = (I + A)^-1 by forward substitution,
+    //      into registers; waves 1..7 meanwhile store the Q exp(G) and M tiles ----
+    // Each lane of wave 0 owns one column c of one 16x16 diagonal block b and
+    // runs the unit lower triangular forward substitution in fp32:
     //   T_bb[r][c] = [r == c] - sum_{j < r} A_bb[r][j] T_bb[j][c]
-    // (rows above c come out exactly 0).
+    // (rows above c come out exactly 0).  It reads only A; the stores read the
+    // Q exp(G) staging rows and M (held in the T region), so the two overlap.
+    // (Every workspace operand is written nontemporally: it is read back only
+    // by the state kernel, after this kernel, so it need not stay in the caches.)
     constexpr int LD = C + 1;
+    float tdiag[16];
     if (wave == 0) {
         const int b = lane >> 4, c = lane & 15;
         const float *Ab = &sm.u.m.r3.A[16 * b][16 * b];
-        float t[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float acc = r == c ? 1.f : 0.f;
 #pragma unroll
-            for (int j = 0; j < r; ++j) acc = __builtin_fmaf(-Ab[r * LD + j], t[j], acc);
-            t[r] = acc;
+            for (int j = 0; j < r; ++j) acc = __builtin_fmaf(-Ab[r * LD + j], tdiag[j], acc);
+            tdiag[r] = acc;
         }
+    } else {
+        constexpr int NS = NTI - 64;   // storing threads
+        const int ts = tid - 64;
+        for (int e = ts; e < (C / 16) * (DK / 32) * 64; e += NS) {
+            const int tile = e >> 6, l = e & 63;
+            const int rt = tile / (DK / 32), kk = tile % (DK / 32);
+            __builtin_nontemporal_store(lds8(&sm.u.m.r1.stage[16 * rt + (l & 15)][32 * kk + 8 * (l >> 4)]),
+                reinterpret_cast<f16x8 *>(w.QG + qg_off + (size_t)e * 8));
+        }
+        for (int e = ts; e < (C / 16) * (C / 32) * 64; e += NS) {   // M: lower triangle incl. diagonal
+            const int tile = e >> 6, l = e & 63;
+            if ((tile & 1) && (tile >> 1) < 2) continue;   // rows < 32, columns >= 32: zero, never read
+            const int r = 16 * (tile >> 1) + (l & 15), i0 = 32 * (tile & 1) + 8 * (l >> 4);
+            f16x8 v;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.u.m.T[16 * b + r][16 * b + c] = t[r];
+            for (int u = 0; u < 8; ++u)
+                v[u] = (_Float16)(i0 + u < r ? sm.u.m.T[r][i0 + u] : i0 + u == r ? sm.mdiag[r] : 0.f);
+            __builtin_nontemporal_store(v, reinterpret_cast<f16x8 *>(w.M + sh * C * C + (size_t)e * 8));
+        }
+    }
+    __syncthreads();
+    // T: the blocks above the block diagonal are zero; wave 0 writes the diagonal blocks
+    for (int e = tid; e < C * C; e += NTI) {
+        const int r = e / C, i = e % C;
+        if ((i >> 4) > (r >> 4)) sm.u.m.T[r][i] = 0.f;
+    }
+    if (wave == 0) {
+        const int b = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.u.m.T[16 * b + r][16 * b + c] = tdiag[r];
     }
     __syncthreads();
     // Off-diagonal blocks.  With D = I + (diagonal blocks of A), N = D^-1 A_off
