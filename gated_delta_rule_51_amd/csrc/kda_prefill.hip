@@ -693,13 +693,18 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
         __syncthreads();
     }
 
-    // ---- W = T (beta K exp(G)) -> LDS stage -> global tiles (waves 0..3);
-    //      T diag(beta) -> global A-operand tiles (waves 4..7) ----
+    // ---- W = T (beta K exp(G)) -> LDS stage -> global A-operand tiles: waves
+    //      w and w + 4 share token row tile w and split W's 32-column tiles
+    //      (all of them on waves 0..3 when K = 32); waves 4..7 also store
+    //      T diag(beta) as A-operand tiles ----
     {
         const int m = lane & 15, kq = lane >> 4;
         const int rt = wave & 3, which = wave >> 2;
         const bool k1 = rt >= 2;   // T rows < 32 vanish for columns >= 32
-        if (which == 0) {
+        constexpr int KT = DK / 32;                 // 32-column tiles of W
+        constexpr int SPLIT = KT >= 2 ? 2 : 1;      // wave groups sharing them
+        if (SPLIT == 2 || which == 0) {
+            const int kt0 = SPLIT == 2 ? which * (KT / 2) : 0;
             f16x8 ta[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -708,21 +713,25 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
                 for (int e = 0; e < 8; ++e) ta[kk][e] = (_Float16)tp[e];
             }
 #pragma unroll
-            for (int ct = 0; ct < DK / 16; ++ct) {
+            for (int c2 = 0; c2 < 2 * KT / SPLIT; ++c2) {
+                const int ct = 2 * kt0 + c2;   // 16-column tile
                 f32x4 acc = mfma_f16(ta[0], lds8(&sm.u.m.KGt[16 * ct + m][kq * 8]), zero4());
                 if (k1) acc = mfma_f16(ta[1], lds8(&sm.u.m.KGt[16 * ct + m][32 + kq * 8]), acc);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) sm.u.m.r1.stage[16 * rt + 4 * kq + jj][16 * ct + m] = (_Float16)acc[jj];
             }
-            // this wave's 16 staged rows -> its A-operand tiles (rt, kk) of W,
-            // with no workgroup barrier (the rows are this wave's own)
+            // this wave's staged block (16 rows, its columns) -> its A-operand
+            // tiles (rt, kk) of W, with no workgroup barrier (the block is its own)
             wave_sync();
-            _Float16 *Wg = w.W + sh * C * DK + (size_t)rt * (DK / 32) * 512;
+            _Float16 *Wg = w.W + sh * C * DK + (size_t)rt * KT * 512;
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk)
+            for (int k2 = 0; k2 < KT / SPLIT; ++k2) {
+                const int kk = kt0 + k2;
                 __builtin_nontemporal_store(lds8(&sm.u.m.r1.stage[16 * rt + m][32 * kk + 8 * kq]),
                     reinterpret_cast<f16x8 *>(Wg + ((size_t)kk * 64 + lane) * 8));
-        } else {
+            }
+        }
+        if (which == 1) {
             // Ut = T diag(beta) V is formed by the state kernel from the v rows
             // it streams; T diag(beta) goes out as A-operand tiles (rt, kk),
             // the zero tile (rt < 2, kk = 1) not stored.
