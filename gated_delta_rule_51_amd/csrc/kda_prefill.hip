@@ -209,11 +209,17 @@ template <int DK, int DV> struct IntraMain {
     } r3;
     float T[C][C + 1];                        // M during the levels, then T = (I + A)^-1
 };
+// Wave-local gate levels 0..2 (K = 128): each wave's 36 operand rows (k P,
+// q P and k S for the four row / column tokens of each level in its own
+// eight tokens), padded like the level rows.
+constexpr int kWlRows = 36;
+
 template <int DK, int DV> struct IntraSmem {
     float beta[C];
     float mdiag[C];   // q_t . k_t, the diagonal of M
     union {
         IntraMain<DK, DV> m;
+        _Float16 wl[8][kWlRows][DK + PADH];
     } u;
 };
 
@@ -243,19 +249,24 @@ template <int ARM> __device__ __forceinline__ void keep_branch() {
 
 // Advance the chains from level LVL-1 to LVL and write this level's operand
 // rows: P[tau] / S[tau] hold (channel 2cp, channel 2cp+1) products as float2.
+// Chains from level LVL-1 to LVL inside a thread's eight tokens (LVL = 1..3).
+template <int LVL> __device__ __forceinline__ void chain_in_eighth(f32x2 (&P)[8], f32x2 (&S)[8]) {
+    constexpr int hb = 1 << (LVL - 1);
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau)   // S first: it reads P of level LVL-1
+        if (((tau >> (LVL - 1)) & 1) == 0) S[tau] *= P[tau | (2 * hb - 1)];
+#pragma unroll
+    for (int tau = 7; tau >= 0; --tau)
+        if ((tau >> (LVL - 1)) & 1) P[tau] *= P[(tau & ~(2 * hb - 1)) + hb - 1];
+}
+
 template <int LVL, int DK, int DV>
 __device__ __forceinline__ void factor_level(f32x2 (&P)[8], f32x2 (&S)[8], const f16x2 (&kr)[8],
                                              const f16x2 (&qr)[8], IntraSmem<DK, DV> &sm, int cp, int e8,
                                              f32x2 &H0, f32x2 &H1) {
     float (*etot)[DK] = eighth_totals(sm);
     if constexpr (LVL >= 1 && LVL <= 3) {
-        constexpr int hb = 1 << (LVL - 1);
-#pragma unroll
-        for (int tau = 0; tau < 8; ++tau)   // S first: it reads P of level LVL-1
-            if (((tau >> (LVL - 1)) & 1) == 0) S[tau] *= P[tau | (2 * hb - 1)];
-#pragma unroll
-        for (int tau = 7; tau >= 0; --tau)
-            if ((tau >> (LVL - 1)) & 1) P[tau] *= P[(tau & ~(2 * hb - 1)) + hb - 1];
+        chain_in_eighth<LVL>(P, S);
     } else if constexpr (LVL == 4) {
         // 16-token blocks = eighths (2j, 2j+1): the partner eighth's total
         const int pe = e8 ^ 1;
@@ -371,6 +382,54 @@ __device__ __forceinline__ void mfma_level(IntraSmem<DK, DV> &sm, int wave, int 
     }
 }
 
+// Levels 0..2 pair tokens inside one aligned block of eight, which with
+// K = 128 is one wave's (the gate thread of lane cp holds channels 2cp, 2cp+1
+// of its eight tokens).  Each wave writes the operand rows of all three
+// levels to its own LDS block and forms its pairs with two 16x16 MFMA tiles
+// (A: k P rows, M: q P rows, against the k S column rows), row / column
+// 4 l + index of the token among the level's four row / column tokens; the
+// valid pairs lie in the three 4x4 diagonal blocks.  No workgroup barrier is
+// needed until the results are scattered.  Returns the two accumulators.
+template <int DK, int DV>
+__device__ __forceinline__ void wave_levels_012(f32x2 (&P)[8], f32x2 (&S)[8], const f16x2 (&kr)[8],
+                                                const f16x2 (&qr)[8], IntraSmem<DK, DV> &sm, int cp, int wave,
+                                                int lane, f32x4 &accA, f32x4 &accM) {
+    static_assert(DK == 128, "one eighth per wave");
+    _Float16 (*wb)[DK + PADH] = sm.u.wl[wave];
+    auto emit = [&](auto lc) {
+        constexpr int L = decltype(lc)::value;
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) {
+            const int idx = ((tau >> (L + 1)) << L) | (tau & ((1 << L) - 1));
+            if ((tau >> L) & 1) {
+                const f16x2 fac = {(_Float16)P[tau][0], (_Float16)P[tau][1]};
+                *reinterpret_cast<f16x2 *>(&wb[4 * L + idx][2 * cp]) = kr[tau] * fac;
+                *reinterpret_cast<f16x2 *>(&wb[12 + 4 * L + idx][2 * cp]) = qr[tau] * fac;
+            } else {
+                const f16x2 fac = {(_Float16)S[tau][0], (_Float16)S[tau][1]};
+                *reinterpret_cast<f16x2 *>(&wb[24 + 4 * L + idx][2 * cp]) = kr[tau] * fac;
+            }
+        }
+    };
+    emit(std::integral_constant<int, 0>{});
+    chain_in_eighth<1>(P, S);
+    emit(std::integral_constant<int, 1>{});
+    chain_in_eighth<2>(P, S);
+    emit(std::integral_constant<int, 2>{});
+    wave_sync();
+    const int m = lane & 15, kq = lane >> 4;
+    const int rm = m < 12 ? m : 0;   // tile rows / columns 12..15 are unused
+    accA = zero4();
+    accM = zero4();
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) {
+        const int c8 = kk * 32 + kq * 8;
+        const f16x8 col = lds8(&wb[24 + rm][c8]);
+        accA = mfma_f16(lds8(&wb[rm][c8]), col, accA);
+        accM = mfma_f16(lds8(&wb[12 + rm][c8]), col, accM);
+    }
+}
+
 template <int DK, int DV, typename IO, bool SCALAR, bool RAW>
 __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -451,11 +510,16 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
             }
         }
     }
-    // A: the diagonal blocks' diagonal and upper triangle are zero (while the loads are in flight)
-    for (int e = tid; e < 4 * 256; e += NTI) {
-        const int b = e >> 8, rr = (e >> 4) & 15, ii = e & 15;
-        if (ii >= rr) sm.u.m.r3.A[16 * b + rr][16 * b + ii] = 0.f;
-    }
+    // A: the diagonal blocks' diagonal and upper triangle are zero (while the
+    // loads are in flight; with K = 128 after the wave-local levels, whose
+    // operand blocks overlay A)
+    auto zero_a_diag = [&]() {
+        for (int e = tid; e < 4 * 256; e += NTI) {
+            const int b = e >> 8, rr = (e >> 4) & 15, ii = e & 15;
+            if (ii >= rr) sm.u.m.r3.A[16 * b + rr][16 * b + ii] = 0.f;
+        }
+    };
+    if constexpr (DK != 128) zero_a_diag();
     if (tid < C) {
         if constexpr (RAW) sm.beta[tid] = tid < L ? sigmoid_f(io_traits<IO>::load(&braw, 0)) : 0.f;
         else sm.beta[tid] = braw;
@@ -527,8 +591,30 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
     __syncthreads();
 
     // ---- levels 0..5: gate factors, then A and M tiles ----
+    // (K = 128: levels 0..2 wave-local, then their pairs scattered into A and M)
+    constexpr int LVL0 = DK == 128 ? 3 : 0;
+    if constexpr (DK == 128) {
+        f32x4 accA, accM;
+        wave_levels_012(P, S, kr, qr, sm, cp, wave, lane, accA, accM);
+        __syncthreads();   // every wave is done with its operand block
+        zero_a_diag();
+        const int m = lane & 15, kq = lane >> 4;
+        // accumulator element jj: tile row 4 kq + jj (level kq, row token index jj),
+        // column m (level m / 4, column token index m % 4)
+        if (kq < 3 && (m >> 2) == kq) {
 #pragma unroll
-    for (int lvl = 0; lvl < 6; ++lvl) {
+            for (int jj = 0; jj < 4; ++jj) {
+                const int tr = insert_bit(jj, kq, 1), tc = insert_bit(m & 3, kq, 0);
+                if ((tr >> (kq + 1)) == (tc >> (kq + 1))) {
+                    const int r = 8 * wave + tr, i = 8 * wave + tc;
+                    sm.u.m.r3.A[r][i] = sm.beta[r] * accA[jj];
+                    sm.u.m.T[r][i] = accM[jj];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int lvl = LVL0; lvl < 6; ++lvl) {
         if (fthread) {
             switch (lvl) {
             case 0: factor_level<0>(P, S, kr, qr, sm, cp, e8, H0, H1); break;
