@@ -17,7 +17,8 @@
 // p with i <= p < r into exp(G_r - G_p) * exp(G_p - G_i), both <= 1, using a
 // hierarchy of aligned blocks: the pair (r, i) belongs to the level of the
 // highest bit in which r and i differ, and the pivot is the last token of the
-// first half of that block.  Each level is one set of 16x16 MFMA tiles.
+// first half of that block.  Each level is one set of 16x16 MFMA tiles (with
+// K = 128 the three levels inside a block of eight tokens are formed per wave).
 //
 // Kernels (all on the caller's stream, no host synchronisation):
 //   meta   : chunk map (sequence, local chunk) per chunk slot, from cu_seqlens
@@ -25,7 +26,8 @@
 //            T = (I + A)^-1 by blocked inversion on fp32 MFMA, W on fp16
 //            MFMA; writes W, T diag(beta), M, Q*exp(G), (K*exp(G_last-G))^T
 //            and exp(G_last) to the workspace (it never reads v)
-//   state  : per (value tile, sequence, value head), sequential over chunks:
+//   state  : per (sequence, value head), its value columns split over wave
+//            groups of one workgroup, sequential over chunks:
 //            Ut = (T diag(beta)) V from the v rows it streams once, U = Ut - W S,
 //            O, state update; reads h0 and writes the final state
 //            at the sequence's dense row or pool slot (sglang PR 30169 digest,
