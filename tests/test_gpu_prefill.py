@@ -108,13 +108,17 @@ def test_scalar_gate_gdn(K, oracle, gate):
     check("gdn-%s" % gate, o, ht, o_ref, ht_ref)
 
 
-@pytest.mark.parametrize("dk,dv", [(64, 64), (32, 32), (128, 64), (64, 128), (32, 128)])
-def test_head_dims(K, oracle, dk, dv):
-    inp = W.make_prefill(62 + dk + dv, [130, 5, 64], 1, 2, dk, dv, h0="random", scale=dk ** -0.5)
+@pytest.mark.parametrize("dk,dv,io", [(64, 64, "bf16"), (32, 32, "bf16"), (128, 64, "bf16"), (64, 128, "bf16"),
+                                      (32, 128, "bf16"), (128, 32, "bf16"), (128, 128, "f32")])
+def test_head_dims(K, oracle, dk, dv, io):
+    """Every compiled (K, V) pairing the kernels specialise on, with K = 128
+    (the per-wave gate levels) against V = 32 (two of four waves stage v) and
+    fp32 io at K = V = 128 (two staging units per thread, fp32 output rows)."""
+    inp = W.make_prefill(62 + dk + dv, [130, 5, 64], 1, 2, dk, dv, io=io, h0="random", scale=dk ** -0.5)
     o, ht = run_dense(K, inp)
     o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=inp.h0,
                                    scale=inp.scale)
-    check("dims-%d-%d" % (dk, dv), o, ht, o_ref, ht_ref)
+    check("dims-%d-%d-%s" % (dk, dv, io), o, ht, o_ref, ht_ref)
 
 
 def test_ragged_and_empty_sequences(K, oracle):
