@@ -866,6 +866,7 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 // waves per CU: one chain of 128 value columns, or two of at most 64.
 // ---------------------------------------------------------------------------
 constexpr int NTS = 512;   // threads of the state kernel per column part
+constexpr long kFewChains = 256;   // at most this many chains: one workgroup per column part
 
 template <int DK, int DV, typename IO> struct StateSmem {
     _Float16 Sh[DV][DK + PADH];   // S^T as fp16 (B operand of W S and Q exp(G) S)
@@ -1212,19 +1213,32 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
 // only the barriers, so they step through the chunks in lockstep and the
 // operand tiles both parts load (W, Q exp(G), M, the key factors, T diag(beta))
 // are fetched from HBM once and served to the second part by the caches.
-template <int DK, int DV, int DVW, typename IO, typename ST>
-__global__ __launch_bounds__(NTS * (DV / DVW)) void state_kernel(PrefillArgs a, Work w) {
+//
+// With PPW = 1 and two column parts, each part is a workgroup of its own
+// instead (used for few chains, where the parts' operand re-reads cost little
+// and an eight-wave barrier is cheaper than a sixteen-wave one); the two
+// parts of a chain get block ids kXcd apart inside one group of kXcd chains,
+// so they run on one XCD and share its L2.
+template <int DK, int DV, int DVW, int PPW, typename IO, typename ST>
+__global__ __launch_bounds__(NTS * PPW) void state_kernel(PrefillArgs a, Work w) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     StateSmem<DK, DVW, IO> *parts = reinterpret_cast<StateSmem<DK, DVW, IO> *>(smem_raw);
     // (sequence rank, head) chains, rank-major: the longest sequences come first
-    const int chain = blockIdx.x;
+    constexpr int NPART = DV / DVW;
+    static_assert(PPW == NPART || PPW == 1, "parts per workgroup");
+    int chain = blockIdx.x, part0 = 0;
+    if constexpr (PPW < NPART) {
+        const int grp = blockIdx.x / (kXcd * NPART), r = blockIdx.x % (kXcd * NPART);
+        part0 = r / kXcd;
+        chain = grp * kXcd + r % kXcd;
+    }
     const int h = chain % a.hv, rank = chain / a.hv;
     if (rank >= a.num_seqs) return;
     const int n = w.seq_order[rank];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int part = wv / 8, wave = wv % 8;
-    StateSmem<DK, DVW, IO> &sm = parts[part];
+    const int part = part0 + wv / 8, wave = wv % 8;
+    StateSmem<DK, DVW, IO> &sm = parts[wv / 8];
     if (wave < 4) state_chain<true, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);    // U waves
     else state_chain<false, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);   // output waves
 }
@@ -1245,16 +1259,17 @@ hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int DK, int DV, int DVW, typename IO, typename ST>
+template <int DK, int DV, int DVW, int PPW, typename IO, typename ST>
 hipError_t launch_state_w(PrefillArgs &a, Work &w, hipStream_t s) {
     // 1-D grid over (sequence rank, head) chains, rank-major; eight waves per column part
     constexpr int NPART = DV / DVW;
-    const size_t smem = NPART * sizeof(StateSmem<DK, DVW, IO>);
-    auto kern = state_kernel<DK, DV, DVW, IO, ST>;
+    const size_t smem = PPW * sizeof(StateSmem<DK, DVW, IO>);
+    auto kern = state_kernel<DK, DV, DVW, PPW, IO, ST>;
     const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     const long chains = (long)a.hv * a.num_seqs;
-    kern<<<dim3((unsigned)chains), NTS * NPART, smem, s>>>(a, w);
+    const long blocks = PPW == NPART ? chains : (chains + kXcd - 1) / kXcd * kXcd * NPART;
+    kern<<<dim3((unsigned)blocks), NTS * PPW, smem, s>>>(a, w);
     return hipGetLastError();
 }
 
@@ -1265,8 +1280,12 @@ hipError_t launch_state_st(PrefillArgs &a, Work &w, hipStream_t s) {
     // chains set the kernel's end), and each part's LDS blocks stay at 64
     // value columns.
     constexpr int DVW = DV == 128 ? 64 : DV;
-    static_assert(DV / DVW == (DV == 128 ? 2 : 1), "column parts");
-    return launch_state_w<DK, DV, DVW, IO, ST>(a, w, s);
+    constexpr int NPART = DV / DVW;
+    static_assert(NPART == (DV == 128 ? 2 : 1), "column parts");
+    if constexpr (NPART > 1) {
+        if ((long)a.hv * a.num_seqs <= kFewChains) return launch_state_w<DK, DV, DVW, 1, IO, ST>(a, w, s);
+    }
+    return launch_state_w<DK, DV, DVW, NPART, IO, ST>(a, w, s);
 }
 
 template <int DK, int DV, typename IO>
