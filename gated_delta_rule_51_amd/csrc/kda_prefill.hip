@@ -909,7 +909,7 @@ __device__ __forceinline__ size_t uniform_off(size_t x) {
 
 // Per-wave part of one (sequence, head) chain; UW selects the role (U wave or
 // output wave).  Both roles pass the same barriers in the same order.
-template <bool UW, bool LOOSE, int DK, int DV, int DVW, typename IO, typename ST>
+template <bool UW, int DK, int DV, int DVW, typename IO, typename ST>
 __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w, StateSmem<DK, DVW, IO> &sm,
                                             int n, int h, int j0, int wave, int lane) {
     // This workgroup owns value columns j0 .. j0 + DVW - 1 of the chain (the
@@ -1137,8 +1137,6 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
             } else {
                 Oacc[ct] = acc;
             }
-            // bound the hoisted LDS reads (register budget of the U waves)
-            if (!LOOSE && (UW || (ct & 1))) __builtin_amdgcn_sched_barrier(0);
         }
         load_x(nxt);
         pin_loads();
@@ -1154,7 +1152,6 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
                     io_traits<IO>::store(&sm.Ost[ow][4 * kq + jj][0], 16 * ct + m, a.scale * Oacc[ct][jj]);
-                if (!LOOSE && (ct & 1)) __builtin_amdgcn_sched_barrier(0);
             }
             load_m(nxt);
             pin_loads();
@@ -1185,7 +1182,6 @@ __device__ __forceinline__ void state_chain(const PrefillArgs &a, const Work &w,
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
                     S[c] = mfma_f16(Ka[kk], lds8(&sm.Vn[16 * (ct0 + c) + m][kk * 32 + kq * 8]), S[c]);
-                if (!LOOSE && (c & 1)) __builtin_amdgcn_sched_barrier(0);
             }
             load_k(nxt);
             pin_loads();
@@ -1239,11 +1235,8 @@ __global__ __launch_bounds__(NTS * PPW, PPW < DV / DVW ? 2 : 4) void state_kerne
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int part = part0 + wv / 8, wave = wv % 8;
     StateSmem<DK, DVW, IO> &sm = parts[wv / 8];
-    // Few chains (one workgroup per part): no scheduling fences and a relaxed
-    // register budget, so independent MFMA chains of a step interleave.
-    constexpr bool LOOSE = PPW < NPART;
-    if (wave < 4) state_chain<true, LOOSE, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);    // U waves
-    else state_chain<false, LOOSE, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);   // output waves
+    if (wave < 4) state_chain<true, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);    // U waves
+    else state_chain<false, DK, DV, DVW, IO, ST>(a, w, sm, n, h, part * DVW, wave, lane);   // output waves
 }
 
 // ---------------------------------------------------------------------------
