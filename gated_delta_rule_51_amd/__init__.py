@@ -143,6 +143,19 @@ def _need(t, name, dtype=None, ndim=None):
         raise ValueError("%s must have %d dims" % (name, ndim))
 
 
+def _on_device(ref, tensors):
+    """Every tensor must be a GPU tensor on ref's device: the kernels take raw
+    device pointers, and a host or foreign-device pointer would be
+    dereferenced on the GPU.  Returns the device."""
+    dev = ref.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be GPU tensors, got a tensor on %s" % dev)
+    for t in tensors:
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on %s, got one on %s" % (dev, t.device))
+    return dev
+
+
 def _io_dtype(q):
     if q.dtype not in _DT:
         raise ValueError("q/k/v must be float32 or bfloat16")
@@ -196,17 +209,17 @@ def _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale, out
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
     _need(initial_state, "initial_state", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
-    dev = q.device
+    dev = _on_device(q, (k, v, *gate, cu_seqlens, initial_state, state_indices))
     N = cu_seqlens.numel() - 1
     T, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     pool = state_indices is not None
+    if pool and initial_state is None:
+        raise ValueError("pool mode needs the pool as initial_state")
     sd = initial_state.dtype if initial_state is not None else (state_dtype or torch.float32)
     desc = prefill_desc(q, v, gate[0], N, sd, scale, initial_state.shape[0] if pool else 0)
     o = torch.empty(T, hv, dv, dtype=q.dtype, device=dev)
     if pool:
-        if initial_state is None:
-            raise ValueError("pool mode needs the pool as initial_state")
         final = initial_state
         fptr = None
     else:
@@ -216,9 +229,10 @@ def _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale, out
     need = workspace_size(desc)
     ws = _workspace(dev, stream, need)
     fn = lib().kda_chunk_prefill_fused_gate if raw else lib().kda_chunk_prefill
-    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate),
-              _ptr(cu_seqlens), _ptr(initial_state), _ptr(state_indices), fptr,
-              _ptr(o), _ptr(ws), ws.numel(), stream))
+    with torch.cuda.device(dev):
+        _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate),
+                  _ptr(cu_seqlens), _ptr(initial_state), _ptr(state_indices), fptr,
+                  _ptr(o), _ptr(ws), ws.numel(), stream))
     return o, final
 
 
@@ -251,14 +265,16 @@ def _decode(q, k, v, gate, state_pool, state_indices, scale, raw):
         _need(t, n, q.dtype, 3)
     _need(state_pool, "state_pool", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
+    dev = _on_device(q, (k, v, *gate, state_pool, state_indices))
     B, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     desc = DecodeDesc(B, hk, hv, dk, dv, _io_dtype(q), _DT[state_pool.dtype],
                       GATE_SCALAR if gate[0].dim() == 2 else GATE_CHANNEL, float(scale), state_pool.shape[0])
-    o = torch.empty(B, hv, dv, dtype=q.dtype, device=q.device)
+    o = torch.empty(B, hv, dv, dtype=q.dtype, device=dev)
     fn = lib().kda_recurrent_decode_fused_gate if raw else lib().kda_recurrent_decode
-    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate),
-              _ptr(state_pool), _ptr(state_indices), _ptr(o), _stream(q.device)))
+    with torch.cuda.device(dev):
+        _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate),
+                  _ptr(state_pool), _ptr(state_indices), _ptr(o), _stream(dev)))
     return o
 
 
@@ -297,6 +313,7 @@ def _decode_multi(q, k, v, gate, cu_seqlens, state_pool, state_indices, cache, u
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
     _need(state_pool, "state_pool", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
+    dev = _on_device(q, (k, v, *gate, cu_seqlens, state_pool, state_indices, cache))
     T, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     N = cu_seqlens.numel() - 1
@@ -304,11 +321,12 @@ def _decode_multi(q, k, v, gate, cu_seqlens, state_pool, state_indices, cache, u
     desc = MultiDecodeDesc(N, T, hk, hv, dk, dv, _io_dtype(q), _DT[state_pool.dtype],
                            GATE_SCALAR if gate[0].dim() == 2 else GATE_CHANNEL, float(scale),
                            state_pool.shape[0], pitch, 1 if update_pool else 0)
-    o = torch.empty(T, hv, dv, dtype=q.dtype, device=q.device)
+    o = torch.empty(T, hv, dv, dtype=q.dtype, device=dev)
     fn = lib().kda_recurrent_decode_multi_fused_gate if raw else lib().kda_recurrent_decode_multi
-    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate), _ptr(cu_seqlens),
-              _ptr(state_pool), _ptr(state_indices), _ptr(cache) if pitch else None, _ptr(o),
-              _stream(q.device)))
+    with torch.cuda.device(dev):
+        _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate), _ptr(cu_seqlens),
+                  _ptr(state_pool), _ptr(state_indices), _ptr(cache) if pitch else None, _ptr(o),
+                  _stream(dev)))
     return o
 
 
@@ -338,13 +356,15 @@ def _decode_packed(qkv, gate, state_pool, state_indices, hk, hv, dk, dv, scale, 
     _need(qkv, "qkv", None, 2)
     _need(state_pool, "state_pool", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
+    dev = _on_device(qkv, (*gate, state_pool, state_indices))
     B = qkv.shape[0]
     desc = DecodeDesc(B, hk, hv, dk, dv, _io_dtype(qkv), _DT[state_pool.dtype],
                       GATE_SCALAR if gate[0].dim() == 2 else GATE_CHANNEL, float(scale), state_pool.shape[0])
-    o = torch.empty(B, hv, dv, dtype=qkv.dtype, device=qkv.device)
+    o = torch.empty(B, hv, dv, dtype=qkv.dtype, device=dev)
     fn = lib().kda_recurrent_decode_packed_fused_gate if raw else lib().kda_recurrent_decode_packed
-    _check(fn(ctypes.byref(desc), _ptr(qkv), *(_ptr(t) for t in gate), _ptr(state_pool), _ptr(state_indices),
-              _ptr(o), _stream(qkv.device)))
+    with torch.cuda.device(dev):
+        _check(fn(ctypes.byref(desc), _ptr(qkv), *(_ptr(t) for t in gate), _ptr(state_pool), _ptr(state_indices),
+                  _ptr(o), _stream(dev)))
     return o
 
 

@@ -223,3 +223,26 @@ def test_packed_decode_errors(L):
     assert L.kda_recurrent_decode_packed(ctypes.byref(d), *bad) == ALIAS
     bad = list(args); bad[0] = fake(1, 8)
     assert L.kda_recurrent_decode_packed(ctypes.byref(d), *bad) == ALIGN
+
+
+def test_binding_rejects_host_tensors():
+    """The Python binding refuses tensors that are not on a GPU before it
+    reaches the library: the kernels would dereference their host pointers."""
+    import torch
+    T, N, B, H, D = 8, 1, 2, 2, 32
+    q = torch.zeros(T, H, D, dtype=torch.bfloat16)
+    g = torch.zeros(T, H, D)
+    beta = torch.zeros(T, H)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        kda.chunk_prefill(q, q, q, g, beta, cu)
+    pool = torch.zeros(4, H, D, D)
+    idx = torch.zeros(B, dtype=torch.int32)
+    qb, gb, bb = q[:B].contiguous(), g[:B].contiguous(), beta[:B].contiguous()
+    with pytest.raises(ValueError, match="GPU tensors"):
+        kda.recurrent_decode(qb, qb, qb, gb, bb, pool, idx)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        kda.recurrent_decode_multi(q, q, q, g, beta, cu, pool, idx[:N].contiguous())
+    qkv = torch.zeros(B, 3 * H * D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        kda.recurrent_decode_packed(qkv, gb, bb, pool, idx, hk=H, hv=H, dk=D, dv=D)

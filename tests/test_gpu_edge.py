@@ -9,7 +9,8 @@ against the fp64 oracle through the C ABI:
 * many short sequences, including more than the meta kernel ranks by length
   (the natural order is kept beyond that count) and more than one scan block;
 * 1200 (sequence, head) chains with 128 value columns (2400 column parts of
-  the state kernel), many of them empty.
+  the state kernel), many of them empty;
+* a host tensor mixed into GPU arguments is refused before any launch.
 """
 import numpy as np
 import pytest
@@ -109,3 +110,17 @@ def test_large_token_count(K, oracle):
     say("T=131072 heads %s: o max-abs %.3e  state rel-L2 %.3e" % (heads, e_o, e_s))
     assert e_o <= O_MAXABS
     assert e_s <= STATE_REL_F32
+
+
+def test_mixed_device_arguments_refused(K):
+    """A host tensor among GPU arguments is refused by the binding (its
+    pointer would be dereferenced on the GPU); nothing is launched."""
+    inp = W.make_prefill(3, [40], 2, 2, 32, 32, h0="random")
+    args = [dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)]
+    for i in range(len(args)):
+        bad = list(args)
+        bad[i] = bad[i].cpu()
+        with pytest.raises(ValueError, match="GPU tensors|must be on"):
+            K.chunk_prefill(*bad)
+    with pytest.raises(ValueError, match="must be on"):
+        K.chunk_prefill(*args, initial_state=dev(inp.h0).cpu())
