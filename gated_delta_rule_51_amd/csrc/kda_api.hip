@@ -102,14 +102,15 @@ kda_status prefill_impl(const kda_prefill_desc *d, const void *q, const void *k,
     if (N == 0) return KDA_OK;
     if (T == 0 && !final_state) return KDA_OK;
 
-    // Grids, all 1-D: intra over (chunk slot, head) items, padded to a
-    // multiple of 8; state over (sequence, head) pairs.
+    // Grids, all 1-D: intra over (chunk slot, head) items; state over
+    // (sequence, head) pairs (at most 256 of them: two column-part
+    // workgroups each, a few hundred in all).
     int dev = 0, max_x = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess)
         return KDA_ERR_HIP;
     const long slots = (T + 63L * N) / 64;
-    const long intra_wgs = (slots * d->hv + 7) / 8 * 8;
+    const long intra_wgs = slots * d->hv;
     const long state_wgs = (long)d->hv * N;   // one workgroup per (sequence, head) chain
     if (intra_wgs > max_x || state_wgs > max_x) return KDA_ERR_UNSUPPORTED;
 

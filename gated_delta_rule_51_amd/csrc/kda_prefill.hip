@@ -439,9 +439,10 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 
     // 1-D grid over (chunk slot, head) items, head fastest, so that resident
     // workgroups read neighbouring tokens of every head (contiguous rows).
-    // Each XCD (ids round-robin over kXcd) takes one contiguous range.
-    const int n_items = w.slots * a.hv, per = (n_items + kXcd - 1) / kXcd;
-    const int item = (int)(blockIdx.x % kXcd) * per + (int)(blockIdx.x / kXcd);
+    // Block ids go round-robin over the XCDs, so each XCD takes every
+    // kXcd-th head of the chunks in flight.
+    const int n_items = w.slots * a.hv;
+    const int item = (int)blockIdx.x;
     if (item >= n_items) return;
     const int slot = item / a.hv, h = item % a.hv;
     const int2 cm = w.chunk_map[slot];
@@ -1246,7 +1247,7 @@ template <int DK, int DV, typename IO>
 hipError_t launch_intra(PrefillArgs &a, Work &w, hipStream_t s) {
     const size_t smem = sizeof(IntraSmem<DK, DV>);
     const long items = (long)w.slots * a.hv;
-    dim3 grid((unsigned)((items + kXcd - 1) / kXcd * kXcd));
+    dim3 grid((unsigned)items);
     auto kern = a.raw_gate ? (a.scalar_gate ? intra_kernel<DK, DV, IO, true, true> : intra_kernel<DK, DV, IO, false, true>)
                            : (a.scalar_gate ? intra_kernel<DK, DV, IO, true, false> : intra_kernel<DK, DV, IO, false, false>);
     const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
