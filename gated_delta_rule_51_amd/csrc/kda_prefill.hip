@@ -143,11 +143,14 @@ __global__ __launch_bounds__(1024) void meta_kernel(const int32_t *cu, int n, Wo
     // start in the first wave of workgroups (ties keep index order).  Counting
     // ranks is O(N^2); beyond kOrderMax sequences the natural order is kept.
     if (n <= kOrderMax) {
+        __shared__ int32_t len[kOrderMax];   // lengths staged once: the rank loop reads LDS
+        for (int s = tid; s < n; s += 1024) len[s] = cu[s + 1] - cu[s];
+        __syncthreads();
         for (int s = tid; s < n; s += 1024) {
-            const int ls = cu[s + 1] - cu[s];
+            const int ls = len[s];
             int rank = 0;
             for (int m = 0; m < n; ++m) {
-                const int lm = cu[m + 1] - cu[m];
+                const int lm = len[m];
                 rank += (lm > ls) || (lm == ls && m < s);
             }
             w.seq_order[rank] = s;
