@@ -35,7 +35,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_prefill", "recurrent_decode", "chunk_prefill_fused_gate",
+__all__ = ["chunk_prefill", "chunk_prefill_noalloc", "recurrent_decode", "chunk_prefill_fused_gate",
            "recurrent_decode_fused_gate", "recurrent_decode_multi", "recurrent_decode_multi_fused_gate",
            "recurrent_decode_packed", "recurrent_decode_packed_fused_gate",
            "workspace_size", "library_path", "KdaError"]
@@ -44,6 +44,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 F32, BF16 = 0, 1
+SCRATCH_BYTES = 256 << 20   # KDA_SCRATCH_BYTES of include/kda.h
 GATE_CHANNEL, GATE_SCALAR = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
@@ -98,6 +99,8 @@ def lib():
         L.kda_chunk_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc)]
         L.kda_chunk_prefill.restype = ctypes.c_int
         L.kda_chunk_prefill.argtypes = [ctypes.POINTER(PrefillDesc)] + [_P] * 11 + [ctypes.c_size_t, _P]
+        L.kda_chunk_prefill_noalloc.restype = ctypes.c_int
+        L.kda_chunk_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillDesc)] + [_P] * 11
         L.kda_recurrent_decode.restype = ctypes.c_int
         L.kda_recurrent_decode.argtypes = [ctypes.POINTER(DecodeDesc)] + [_P] * 9
         L.kda_chunk_prefill_fused_gate.restype = ctypes.c_int
@@ -203,7 +206,7 @@ def _gate_args(q, g, beta, raw):
 
 
 def _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale, output_final_state,
-             state_dtype, raw):
+             state_dtype, raw, noalloc=False):
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype, 3)
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
@@ -226,6 +229,12 @@ def _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale, out
         final = torch.empty(N, hv, dv, dk, dtype=sd, device=dev) if output_final_state else None
         fptr = _ptr(final)
     stream = _stream(dev)
+    if noalloc:   # the library's own workspace
+        with torch.cuda.device(dev):
+            _check(lib().kda_chunk_prefill_noalloc(
+                ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in gate), _ptr(cu_seqlens),
+                _ptr(initial_state), _ptr(state_indices), fptr, _ptr(o), stream))
+        return o, final
     need = workspace_size(desc)
     ws = _workspace(dev, stream, need)
     fn = lib().kda_chunk_prefill_fused_gate if raw else lib().kda_chunk_prefill
@@ -248,6 +257,17 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_ind
     gate = _gate_args(q, g, beta, None)
     return _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale,
                     output_final_state, state_dtype, False)
+
+
+def chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_indices=None,
+                          scale=1.0, output_final_state=True, state_dtype=None):
+    """chunk_prefill through kda_chunk_prefill_noalloc: the library's own
+    per-GPU workspace of SCRATCH_BYTES is used, so the library allocates
+    nothing (o and a dense final state are still allocated here).  Calls that
+    overlap in time on one GPU race on that workspace."""
+    gate = _gate_args(q, g, beta, None)
+    return _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale,
+                    output_final_state, state_dtype, False, noalloc=True)
 
 
 def chunk_prefill_fused_gate(q, k, v, gate_x, A_log, dt_bias, beta_x, cu_seqlens, *,

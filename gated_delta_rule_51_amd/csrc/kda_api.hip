@@ -2,8 +2,17 @@
 // Declarations and the contract live in include/kda.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_internal.h"
+
+// Workspace of the allocation-free prefill entry point: one copy of this
+// array per GPU, placed by the code-object loader when the library is first
+// used on that GPU and held until the process ends.  Host code never passes
+// its name to a kernel (on the host it is only a stand-in); it uses the
+// device address looked up once per device by scratch_ptr().
+static __device__ __align__(256) unsigned char scratch[KDA_SCRATCH_BYTES];
 
 namespace {
 
@@ -272,6 +281,24 @@ kda_status multi_decode_impl(const kda_multi_decode_desc *d, const void *q, cons
     return hip_status(kda::launch_decode_multi(a, static_cast<hipStream_t>(stream)));
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU holds its own copy at its own
+// address).  nullptr on failure.
+void *scratch_ptr() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *ptrs[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -315,6 +342,22 @@ kda_status kda_chunk_prefill_fused_gate(const kda_prefill_desc *d, const void *q
     const GateIn gi{gate_x, beta_x, A_log, dt_bias, true};
     return prefill_impl(d, q, k, v, gi, cu_seqlens, state, state_indices, final_state, o, workspace,
                         workspace_bytes, stream);
+}
+
+kda_status kda_chunk_prefill_noalloc(const kda_prefill_desc *d, const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta, const int32_t *cu_seqlens,
+                                     void *state, const int32_t *state_indices, void *final_state, void *o,
+                                     void *stream) {
+    // Sizes beyond the array are refused before any HIP call.
+    const kda_status st = check_desc(d);
+    if (st != KDA_OK) return st;
+    if (kda::prefill_workspace_bytes(d->num_seqs, d->total_tokens, d->hv, d->dk, d->dv) > KDA_SCRATCH_BYTES)
+        return KDA_ERR_WORKSPACE;
+    void *ws = scratch_ptr();
+    if (!ws) return KDA_ERR_HIP;
+    const GateIn gi{g, beta, nullptr, nullptr, false};
+    return prefill_impl(d, q, k, v, gi, cu_seqlens, state, state_indices, final_state, o, ws, KDA_SCRATCH_BYTES,
+                        stream);
 }
 
 kda_status kda_recurrent_decode(const kda_decode_desc *d, const void *q, const void *k, const void *v,

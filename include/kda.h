@@ -159,6 +159,33 @@ kda_status kda_chunk_prefill_fused_gate(const kda_prefill_desc *desc,
                                         void *workspace, size_t workspace_bytes,
                                         void *stream);
 
+/*
+ * Allocation-free chunked prefill, for callers that cannot allocate device
+ * memory around the call: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  It is kda_chunk_prefill with the
+ * workspace taken from a buffer the library holds itself: a device array of
+ * KDA_SCRATCH_BYTES per GPU, placed when the library is first used on that
+ * GPU and held until the process ends.  This call allocates and frees
+ * nothing; its first call on a device looks the array's address up once.
+ *   Limit: kda_chunk_prefill_workspace_size(desc) <= KDA_SCRATCH_BYTES,
+ *   else KDA_ERR_WORKSPACE with nothing launched.  At dk = dv = 128 the
+ *   workspace is about 64.5 KB per (64-token chunk, value head) plus a few
+ *   bytes per sequence: e.g. 8,000 tokens of one sequence at 32 value heads.
+ *   Concurrency: every call on one GPU uses that GPU's one array.  Calls
+ *   ordered on one stream are safe; calls that overlap in time on one GPU
+ *   (two streams, two host threads) race and give undefined results.
+ *   Nothing in the array needs to start at zero: each call writes every
+ *   workspace byte it later reads.
+ * Arguments, layouts, pool mode and errors are those of kda_chunk_prefill.
+ */
+#define KDA_SCRATCH_BYTES ((size_t)256 << 20)
+kda_status kda_chunk_prefill_noalloc(const kda_prefill_desc *desc,
+                                     const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta,
+                                     const int32_t *cu_seqlens,
+                                     void *state, const int32_t *state_indices,
+                                     void *final_state, void *o, void *stream);
+
 /* Host-side description of one decode call. */
 typedef struct {
     int32_t batch;        /* B >= 0 requests, one token each                  */

@@ -108,6 +108,23 @@ def test_workspace_size(L):
     assert b >= a
 
 
+def test_noalloc_limits(L):
+    """kda_chunk_prefill_noalloc: descriptor errors and a workspace beyond the
+    library's array are refused from host values alone, before the array's
+    device address is looked up (so these return without any HIP call)."""
+    assert L.kda_chunk_prefill_noalloc(None, *([None] * 11)) == NULL
+    assert L.kda_chunk_prefill_noalloc(ctypes.byref(desc(dk=48)), *([None] * 11)) == UNSUP
+    big = desc(num_seqs=1, total_tokens=9000, hk=32, hv=32)
+    assert L.kda_chunk_prefill_workspace_size(ctypes.byref(big)) > kda.SCRATCH_BYTES
+    args = [fake(i) for i in range(1, 12)]
+    assert L.kda_chunk_prefill_noalloc(ctypes.byref(big), *args) == WS
+    fits = desc(num_seqs=1, total_tokens=8000, hk=32, hv=32)
+    assert L.kda_chunk_prefill_workspace_size(ctypes.byref(fits)) <= kda.SCRATCH_BYTES
+    hdr = open(HEADER).read()
+    assert "#define KDA_SCRATCH_BYTES ((size_t)256 << 20)" in hdr
+    assert kda.SCRATCH_BYTES == 256 << 20
+
+
 def ddesc(**kw):
     d = dict(batch=4, hk=2, hv=4, dk=128, dv=128, io_dtype=1, state_dtype=0, gate=0, scale=1.0,
              num_slots=16)
