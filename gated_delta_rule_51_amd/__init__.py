@@ -38,7 +38,7 @@ import torch
 __all__ = ["chunk_prefill", "chunk_prefill_noalloc", "recurrent_decode", "chunk_prefill_fused_gate",
            "recurrent_decode_fused_gate", "recurrent_decode_multi", "recurrent_decode_multi_fused_gate",
            "recurrent_decode_packed", "recurrent_decode_packed_fused_gate",
-           "workspace_size", "library_path", "KdaError"]
+           "workspace_size", "release_workspaces", "library_path", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -146,6 +146,46 @@ def _need(t, name, dtype=None, ndim=None):
         raise ValueError("%s must have %d dims" % (name, ndim))
 
 
+def _rows(t, name, n, tail):
+    """t must be [>= n, *tail]: rows past n (a padded batch) are allowed and
+    never read; every other size must match exactly."""
+    if t is None:
+        return
+    if t.dim() != 1 + len(tail) or t.shape[0] < n or tuple(t.shape[1:]) != tuple(tail):
+        raise ValueError("%s must have shape [>= %d, %s], got %s"
+                         % (name, n, ", ".join(str(x) for x in tail), tuple(t.shape)))
+
+
+def _gate_shapes(gate, raw, n, hv, dk):
+    """g or raw x [>= n, hv, dk] (per-channel gate) or [>= n, hv] (scalar
+    gate); beta or raw b [>= n, hv]; A_log, dt_bias [hv, dk] or [hv]."""
+    g = gate[0]
+    if g.dim() not in (2, 3):
+        raise ValueError("%s must be [T, Hv, K] or [T, Hv]" % ("gate_x" if raw else "g"))
+    tail = (hv, dk) if g.dim() == 3 else (hv,)
+    _rows(g, "gate_x" if raw else "g", n, tail)
+    b = gate[3] if raw else gate[1]
+    _rows(b, "beta_x" if raw else "beta", n, (hv,))
+    if raw:
+        for t, name in ((gate[1], "A_log"), (gate[2], "dt_bias")):
+            if tuple(t.shape) != tail:
+                raise ValueError("%s must have shape %s, got %s" % (name, tail, tuple(t.shape)))
+
+
+def _head_shapes(q, k, v):
+    """q, k [n, hk, dk] (k may hold padding rows), v [>= n, hv, dv] with hv a
+    multiple of hk.  Returns (n, hk, dk, hv, dv)."""
+    n, hk, dk = q.shape
+    _rows(k, "k", n, (hk, dk))
+    if v.dim() != 3:
+        raise ValueError("v must be [T, Hv, V]")
+    hv, dv = v.shape[1], v.shape[2]
+    _rows(v, "v", n, (hv, dv))
+    if hk <= 0 or hv % hk != 0:
+        raise ValueError("value heads (%d) must be a multiple of key heads (%d)" % (hv, hk))
+    return n, hk, dk, hv, dv
+
+
 def _on_device(ref, tensors):
     """Every tensor must be a GPU tensor on ref's device: the kernels take raw
     device pointers, and a host or foreign-device pointer would be
@@ -178,15 +218,32 @@ def workspace_size(desc: PrefillDesc) -> int:
 
 # One workspace per (device, stream); calls ordered on one stream may share it.
 _WS = {}
+# Workspaces replaced by a larger one.  They are kept alive: a HIP graph
+# captured earlier on that stream still writes to the address it recorded,
+# and freeing the buffer would hand that memory to other tensors.  Growth is
+# at least twofold, so they hold at most as many bytes as the live ones.
+_WS_RETIRED = []
 
 
 def _workspace(device, stream, nbytes):
     key = (device.index, stream)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        size = max(nbytes, 256)
+        if ws is not None:
+            _WS_RETIRED.append(ws)
+            size = max(size, 2 * ws.numel())
+        ws = torch.empty(size, dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws
+
+
+def release_workspaces():
+    """Free every prefill workspace the binding holds (the current ones and
+    those kept for captured graphs).  Only safe once no captured graph that
+    contains a prefill will be replayed again."""
+    _WS.clear()
+    _WS_RETIRED.clear()
 
 
 def _gate_args(q, g, beta, raw):
@@ -212,13 +269,24 @@ def _prefill(q, k, v, gate, cu_seqlens, initial_state, state_indices, scale, out
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
     _need(initial_state, "initial_state", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
-    dev = _on_device(q, (k, v, *gate, cu_seqlens, initial_state, state_indices))
+    T, hk, dk, hv, dv = _head_shapes(q, k, v)
+    _gate_shapes(gate, raw, T, hv, dk)
     N = cu_seqlens.numel() - 1
-    T, hk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
+    if N < 0:
+        raise ValueError("cu_seqlens must hold N + 1 >= 1 offsets")
     pool = state_indices is not None
     if pool and initial_state is None:
         raise ValueError("pool mode needs the pool as initial_state")
+    if initial_state is not None:
+        if pool:
+            if initial_state.shape[0] < 1:
+                raise ValueError("the pool must have at least one row")
+            _rows(initial_state, "state pool", 1, (hv, dv, dk))
+        else:
+            _rows(initial_state, "initial_state", N, (hv, dv, dk))
+    if pool:
+        _rows(state_indices, "state_indices", N, ())
+    dev = _on_device(q, (k, v, *gate, cu_seqlens, initial_state, state_indices))
     sd = initial_state.dtype if initial_state is not None else (state_dtype or torch.float32)
     desc = prefill_desc(q, v, gate[0], N, sd, scale, initial_state.shape[0] if pool else 0)
     o = torch.empty(T, hv, dv, dtype=q.dtype, device=dev)
@@ -285,9 +353,11 @@ def _decode(q, k, v, gate, state_pool, state_indices, scale, raw):
         _need(t, n, q.dtype, 3)
     _need(state_pool, "state_pool", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
+    B, hk, dk, hv, dv = _head_shapes(q, k, v)
+    _gate_shapes(gate, raw, B, hv, dk)
+    _rows(state_pool, "state_pool", 1, (hv, dv, dk))
+    _rows(state_indices, "state_indices", B, ())
     dev = _on_device(q, (k, v, *gate, state_pool, state_indices))
-    B, hk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
     desc = DecodeDesc(B, hk, hv, dk, dv, _io_dtype(q), _DT[state_pool.dtype],
                       GATE_SCALAR if gate[0].dim() == 2 else GATE_CHANNEL, float(scale), state_pool.shape[0])
     o = torch.empty(B, hv, dv, dtype=q.dtype, device=dev)
@@ -333,10 +403,14 @@ def _decode_multi(q, k, v, gate, cu_seqlens, state_pool, state_indices, cache, u
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
     _need(state_pool, "state_pool", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
-    dev = _on_device(q, (k, v, *gate, cu_seqlens, state_pool, state_indices, cache))
-    T, hk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
+    T, hk, dk, hv, dv = _head_shapes(q, k, v)
+    _gate_shapes(gate, raw, T, hv, dk)
     N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens must hold N + 1 >= 1 offsets")
+    _rows(state_pool, "state_pool", 1, (hv, dv, dk))
+    _rows(state_indices, "state_indices", N, ())
+    dev = _on_device(q, (k, v, *gate, cu_seqlens, state_pool, state_indices, cache))
     pitch = _cache_pitch(cache, N, hv, dv, dk, state_pool.dtype)
     desc = MultiDecodeDesc(N, T, hk, hv, dk, dv, _io_dtype(q), _DT[state_pool.dtype],
                            GATE_SCALAR if gate[0].dim() == 2 else GATE_CHANNEL, float(scale),
@@ -376,8 +450,13 @@ def _decode_packed(qkv, gate, state_pool, state_indices, hk, hv, dk, dv, scale, 
     _need(qkv, "qkv", None, 2)
     _need(state_pool, "state_pool", None, 4)
     _need(state_indices, "state_indices", torch.int32, 1)
-    dev = _on_device(qkv, (*gate, state_pool, state_indices))
     B = qkv.shape[0]
+    if hk <= 0 or hv % hk != 0:
+        raise ValueError("value heads (%d) must be a multiple of key heads (%d)" % (hv, hk))
+    _gate_shapes(gate, raw, B, hv, dk)
+    _rows(state_pool, "state_pool", 1, (hv, dv, dk))
+    _rows(state_indices, "state_indices", B, ())
+    dev = _on_device(qkv, (*gate, state_pool, state_indices))
     desc = DecodeDesc(B, hk, hv, dk, dv, _io_dtype(qkv), _DT[state_pool.dtype],
                       GATE_SCALAR if gate[0].dim() == 2 else GATE_CHANNEL, float(scale), state_pool.shape[0])
     o = torch.empty(B, hv, dv, dtype=qkv.dtype, device=dev)
