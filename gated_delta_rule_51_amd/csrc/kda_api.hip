@@ -177,14 +177,17 @@ kda_status decode_impl(const kda_decode_desc *d, const void *q, const void *k, c
     for (const R &r : ins)
         if (overlap(o, o_b, r.p, r.n)) return KDA_ERR_ALIAS;
 
-    // Grid (hv x dv / tile, B) must fit the device's per-axis limits.
-    int dev = 0, max_x = 0, max_y = 0;
+    // Grid (hv x dv / tile, requests per z slab, z slabs) must fit the
+    // device's per-axis limits.
+    int dev = 0, max_x = 0, max_y = 0, max_z = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess)
+        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_z, hipDeviceAttributeMaxGridDimZ, dev) != hipSuccess)
         return KDA_ERR_HIP;
     const long xdim = (long)d->hv * (d->dv / kda::decode_tile(d->dv));
-    if ((long)d->batch > max_y || xdim > max_x) return KDA_ERR_UNSUPPORTED;
+    if (xdim > max_x || kda::decode_grid_y(d->batch) > max_y || kda::decode_grid_z(d->batch) > max_z)
+        return KDA_ERR_UNSUPPORTED;
 
     kda::DecodeArgs a{};
     a.q = q; a.k = k; a.v = v; a.state = state_pool;
@@ -250,13 +253,15 @@ kda_status multi_decode_impl(const kda_multi_decode_desc *d, const void *q, cons
     if (overlap(cache, cache_b, o, o_b)) return KDA_ERR_ALIAS;
     if (T == 0) return KDA_OK;   // every request is empty: nothing is read or written
 
-    int dev = 0, max_x = 0, max_y = 0;
+    int dev = 0, max_x = 0, max_y = 0, max_z = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess)
+        hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_z, hipDeviceAttributeMaxGridDimZ, dev) != hipSuccess)
         return KDA_ERR_HIP;
     const long xdim = (long)d->hv * (d->dv / kda::decode_tile(d->dv));
-    if ((long)d->batch > max_y || xdim > max_x) return KDA_ERR_UNSUPPORTED;
+    if (xdim > max_x || kda::decode_grid_y(d->batch) > max_y || kda::decode_grid_z(d->batch) > max_z)
+        return KDA_ERR_UNSUPPORTED;
 
     kda::DecodeArgs a{};
     a.q = q; a.k = k; a.v = v; a.state = state_pool;

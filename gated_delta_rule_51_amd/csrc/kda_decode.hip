@@ -10,10 +10,12 @@
 // given k, q, g), and writes the rows back in place.  The grid keeps batch and
 // head on separate axes (sglang PR 37317 digest, 实现拆解 item 1: folding them
 // into one axis overflowed the 65535 limit at large decode batches): x runs
-// over (head, value tile), head-major, and y over the batch, so resident
-// workgroups stream the contiguous [Hv, V, K] block of one pool row.  A
-// negative slot index selects the last pool row (PR 30169 digest, 实现拆解
-// item 3).
+// over (head, value tile), head-major, so consecutive workgroups stream the
+// contiguous [Hv, V, K] block of one pool row, and the batch is spread over
+// y and z (request b = y + z * gridDim.y), so it is not held to one axis's
+// 65535 either (the digest's 风险与影响 item 5 notes that per-axis limit after
+// the split).  A negative slot index selects the last pool row (PR 30169
+// digest, 实现拆解 item 3).
 //
 // Memory-bound: the state row block is read once and written once with
 // 16-byte nontemporal accesses that are contiguous across the workgroup.
@@ -181,7 +183,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int r0 = tid / R::LPR;
     constexpr int NT_MAX = 128 / BV;
     const int nt = a.dv / BV;   // value tiles per head (1 when BV = dv)
-    const int b = blockIdx.y;
+    const int b = (int)blockIdx.y + (int)blockIdx.z * (int)gridDim.y;   // request
+    if (b >= a.batch) return;   // the last z slab may be partly empty
     const int h = NT_MAX == 1 ? (int)blockIdx.x : (int)blockIdx.x / nt;
     const int j0 = NT_MAX == 1 ? 0 : ((int)blockIdx.x % nt) * BV;
     const int hk_idx = h / (a.hv / a.hk);
@@ -217,7 +220,8 @@ __global__ __launch_bounds__(256) void multi_decode_kernel(DecodeArgs a) {
     const int r0 = tid / R::LPR;
     constexpr int NT_MAX = 128 / BV;
     const int nt = a.dv / BV;
-    const int b = blockIdx.y;
+    const int b = (int)blockIdx.y + (int)blockIdx.z * (int)gridDim.y;   // request
+    if (b >= a.batch) return;   // the last z slab may be partly empty
     const int h = NT_MAX == 1 ? (int)blockIdx.x : (int)blockIdx.x / nt;
     const int j0 = NT_MAX == 1 ? 0 : ((int)blockIdx.x % nt) * BV;
     const int hk_idx = h / (a.hv / a.hk);
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(256) void multi_decode_kernel(DecodeArgs a) {
 template <int DK, int BV, typename IO, typename ST, bool SCALAR>
 static hipError_t launch_t(const DecodeArgs &a, bool multi, hipStream_t stream) {
     // The state block is touched once per call: stream it past the caches.
-    dim3 grid(a.hv * (a.dv / BV), a.batch);
+    dim3 grid(a.hv * (a.dv / BV), decode_grid_y(a.batch), decode_grid_z(a.batch));
     if (multi) {
         if (a.raw_gate)
             multi_decode_kernel<DK, BV, IO, ST, SCALAR, true><<<grid, 256, 0, stream>>>(a);
@@ -298,6 +302,13 @@ static hipError_t launch_any(const DecodeArgs &a, bool multi, hipStream_t stream
     case 64: return launch_v<64>(a, bv, multi, stream);
     default: return launch_v<128>(a, bv, multi, stream);
     }
+}
+
+// Batch split over grid y and z: z slabs of at most 65535 requests each.
+int decode_grid_z(int batch) { return batch <= 0 ? 1 : (batch + 65534) / 65535; }
+int decode_grid_y(int batch) {
+    const int z = decode_grid_z(batch);
+    return batch <= 0 ? 1 : (batch + z - 1) / z;
 }
 
 // Whole head per workgroup (up to 128 value rows): measured fastest on MI355X

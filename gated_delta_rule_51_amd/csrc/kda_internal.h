@@ -1,4 +1,4 @@
-// Internal launch interface between the C ABI (kda_api.cpp) and the kernels.
+// Internal launch interface between the C ABI (kda_api.hip) and the kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,6 +32,8 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeArgs &a, hipStream_t stream);
 int decode_tile(int dv);
+int decode_grid_y(int batch);   // requests per z slab of the decode grid
+int decode_grid_z(int batch);   // z slabs
 
 // Chunked prefill.  Chunk size and the chunk-slot bound are fixed here.
 constexpr int kChunk = 64;

@@ -38,12 +38,28 @@
  *     the call describes (a batch padded to a captured size), and rows past
  *     the described count are never read (the KDA prefill digest, sglang
  *     PR 27488, 实现拆解 item 3, trims padded g and beta to q's token count).
- *   - Not checked (preconditions): device index values lie in [-1, slots-1]
+ *   - Not checked (preconditions): device index values lie in [-1, slots-2]
  *     and are unique apart from -1; g is finite and <= 0; cu_seqlens is
  *     non-decreasing with cu[0] = 0 and cu[N] = total_tokens.
  *   - GQA: value head h reads key head h / (hv / hk); hv % hk == 0.
  *   - Supported sizes: dk, dv in {32, 64, 128}.  io dtype f32 or bf16; state
  *     dtype f32 or bf16.  Accumulation is fp32.
+ *   - Prefill precision.  The prefill's matrix-core operands are fp16 (IEEE
+ *     binary16: 11-bit significand, largest finite 65504, normal down to
+ *     2^-14): q, k and v, the gate-scaled key and query rows, T = (I + A)^-1,
+ *     W, M, the state entering each chunk and the residual U are rounded to
+ *     fp16 before each product; products accumulate in fp32 and the carried
+ *     state is fp32.  bf16 inputs convert to fp16 exactly within its range.
+ *     fp16 rather than bf16 keeps the final-state error near 3e-4 relative
+ *     (bf16 operands: about 2.4e-3).  Preconditions (not checked): v, the
+ *     initial states and every state and residual the recurrence reaches stay
+ *     below 65504 in magnitude (beyond it the results overflow to inf);
+ *     magnitudes below 2^-14 keep fewer significant bits.  fp32 io is
+ *     accepted, but its prefill results carry the same fp16-operand rounding
+ *     (about 3e-4 relative on states, not fp32's 1e-7).  The decode entry
+ *     points compute in fp32 throughout.
+ *   - Pool slots: a real request's index must lie in [0, num_slots - 2]; the
+ *     last slot is the padding sentinel that every negative index selects.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -97,7 +113,13 @@ typedef struct {
 size_t kda_chunk_prefill_workspace_size(const kda_prefill_desc *desc);
 
 /*
- * Chunked prefill over packed sequences (chunk size 64).
+ * Chunked prefill over packed sequences (chunk size 64): the chunk pipeline
+ * of the KDA prefill digest (sglang PR 27488, 实现拆解: a per-chunk gate
+ * cumsum prologue, the KKT-inverse + U/W step, the state (h) step and the
+ * output (o) step, chunked over cu_seqlens; 关键源码片段: the pipeline entry
+ * chunk_kda_cutedsl returns o and the final state), with the pool-state I/O
+ * of the pool-mode digest (PR 30169, 实现拆解 items 1-2: initial states read
+ * from and final states written to state_indices[seq] of a pool, in place).
  *   q, k        [T, hk, dk]  io dtype (callers pass L2-normalised q, k)
  *   v           [T, hv, dv]  io dtype
  *   g           [T, hv, dk] (CHANNEL) or [T, hv] (SCALAR), fp32, <= 0
@@ -196,14 +218,21 @@ typedef struct {
 } kda_decode_desc;
 
 /*
- * One-token recurrent decode for B requests against a state pool, in place.
+ * One-token recurrent decode for B requests against a state pool, in place:
+ * the packed KDA decode of the FLA/MoE shape-limits digest (sglang PR 37317,
+ * 实现拆解 item 1: fused_recurrent_kda_packed_decode, one recurrence step per
+ * request and value head, its grid split so batch and head are separate
+ * axes), reading and writing pool rows by index with the padding sentinel of
+ * the pool-mode digest (PR 30169, 实现拆解 item 3).
  *   q, k  [B, hk, dk] io dtype;  v [B, hv, dv] io dtype
  *   g     [B, hv, dk] (CHANNEL) or [B, hv] (SCALAR) fp32;  beta [B, hv] fp32
  *   state_pool     [num_slots, hv, dv, dk] state dtype, read and written in place
  *   state_indices  [B] int32; an index < 0 selects slot num_slots - 1
  *   o     [B, hv, dv] io dtype
- * The launch grid is (hv x dv / tile, B): head (with value tile) on x and
- * batch on y, so batch and head stay on separate axes.
+ * The launch grid is (hv x dv / tile, ceil(B / Z), Z) with Z = ceil(B / 65535):
+ * head (with value tile) on x and the batch over y and z, so batch and head
+ * stay on separate axes and no product of the two, nor the batch alone,
+ * meets an axis limit (B up to 2^31 - 1).
  */
 kda_status kda_recurrent_decode(const kda_decode_desc *desc,
                                 const void *q, const void *k, const void *v,
@@ -279,7 +308,7 @@ typedef struct {
  *                  when cache_pitch is 0; steps at or beyond cache_pitch are
  *                  not cached; must not overlap any other argument
  *   o     [T, hv, dv] io dtype
- * The grid is (hv x dv / tile, N) as for kda_recurrent_decode.  A request
+ * The grid is (hv x dv / tile, ceil(N / Z), Z) as for kda_recurrent_decode.  A request
  * with no tokens writes nothing.  Not checked (preconditions, besides those of
  * kda_chunk_prefill): indices of requests with update_pool set are unique.
  */
