@@ -122,13 +122,38 @@ def cpu_baseline(pre, dec, reps=5, nreq=1024):
         tds.append(time.perf_counter() - t)
     td = statistics.median(tds)
     hv = dec.v.shape[1]
+    # one thread, on the first `h1` heads of every sequence (heads are
+    # independent units of equal cost), scaled to all heads
+    h1 = 4
+    sel = lambda x: x[:, :h1].contiguous()
+    t = time.perf_counter()
+    O.prefill(sel(pre.q), sel(pre.k), sel(pre.v), sel(pre.g), sel(pre.beta), pre.cu_seqlens, h0=sel(h0),
+              nthreads=1)
+    t1 = (time.perf_counter() - t) * hv / h1
     return {
         "value": T / tp, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "sample": "fp64 C oracle (OpenMP over sequence-head units): full prefill batch "
                   "(%d tokens x 32 heads), median of %d runs = %.2f s; decode: first %d of 4096 "
-                  "requests, median of 3 runs = %.3f s" % (T, reps, tp, nreq, td),
+                  "requests, median of 3 runs = %.3f s; one thread: the first %d heads of the "
+                  "prefill batch, scaled to 32 heads" % (T, reps, tp, nreq, td, h1),
         "decode_states_per_s": nreq * hv / td,
+        "one_thread_value": T / t1,
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
