@@ -183,6 +183,54 @@ def kimi_prefill_16seq(seed=4):
                         pool_slots=32)
 
 
+def gdn_pool_page(seed=11, state_dtype="f32", pad_one=False):
+    """The GDN pool-mode test recipe of the sglang PR 30169 digest (key-code
+    test): 5 sequences of randint(1, 130) tokens, Hk = 4, Hv = 8, K = V = 128,
+    bf16 q, k (N(0,1) rounded to bf16, L2-normalised in fp32, rounded again)
+    and v; raw a, b ~ N(0,1) in bf16 per (token, value head); A ~ U(0, 16),
+    A_log = log A; dt log-uniform on [1e-3, 0.1] clamped at 1e-4, dt_bias its
+    inverse softplus; the scalar gate g = -exp(A_log) softplus(a + dt_bias)
+    and beta = sigmoid(b) in fp32; dense initial states 0.05 N(0,1) in the
+    state dtype, scattered into a 64-slot pool of 0.05 N(0,1) rows at
+    randperm(64)[:5].  The draws follow the page's order from one seeded CPU
+    generator (the page draws on the GPU, whose stream differs).  With
+    pad_one, the last sequence's index becomes -1 (the sentinel, last slot),
+    whose row then holds that sequence's initial state."""
+    gen = _gen(seed)
+    n, hk, hv, d = 5, 4, 8, 128
+    lens = torch.randint(1, 130, (n,), generator=gen, dtype=torch.int32)
+    cu = cu_from_lengths(lens)
+    T = int(cu[-1])
+    bf = torch.bfloat16
+    q = torch.randn(T, hk, d, generator=gen).to(bf)
+    k = torch.randn(T, hk, d, generator=gen).to(bf)
+    v = torch.randn(T, hv, d, generator=gen).to(bf)
+    q = torch.nn.functional.normalize(q.float(), p=2, dim=-1).to(bf)
+    k = torch.nn.functional.normalize(k.float(), p=2, dim=-1).to(bf)
+    a = torch.randn(T, hv, generator=gen).to(bf)
+    b = torch.randn(T, hv, generator=gen).to(bf)
+    A = torch.rand(hv, generator=gen) * 16.0
+    A_log = torch.log(A)
+    lo, hi = math.log(1e-3), math.log(0.1)
+    dt = torch.exp(torch.rand(hv, generator=gen) * (hi - lo) + lo).clamp_min(1e-4)
+    dt_bias = dt + torch.log(-torch.expm1(-dt))
+    g = -A_log.exp()[None] * torch.nn.functional.softplus(a.float() + dt_bias[None])
+    beta = torch.sigmoid(b.float())
+    sd = DTYPES[state_dtype]
+    h0 = (torch.randn(n, hv, d, d, generator=gen) * 0.05).to(sd)
+    num_slots = 64
+    pool = (torch.randn(num_slots, hv, d, d, generator=gen) * 0.05).to(sd)
+    slots = torch.randperm(num_slots, generator=gen)[:n].to(torch.int32)
+    if pad_one:
+        slots[-1] = -1
+    rows = torch.where(slots < 0, torch.full_like(slots, num_slots - 1), slots).long()
+    pool[rows] = h0
+    return Prefill(q, k, v, g.contiguous(), beta.contiguous(), cu, h0=h0, pool=pool, indices=slots,
+                   meta=dict(seed=seed, hk=hk, hv=hv, dk=d, dv=d, io="bf16", gate="gdn-page",
+                             scalar_gate=True, state_dtype=state_dtype, T=T),
+                   gx=a, A_log=A_log.float(), dt_bias=dt_bias.float(), bx=b)
+
+
 @dataclass
 class Decode:
     q: torch.Tensor

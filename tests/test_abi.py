@@ -263,3 +263,65 @@ def test_binding_rejects_host_tensors():
     qkv = torch.zeros(B, 3 * H * D, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensors"):
         kda.recurrent_decode_packed(qkv, gb, bb, pool, idx, hk=H, hv=H, dk=D, dv=D)
+
+
+def test_binding_rejects_bad_shapes():
+    """Shape mismatches are refused by the binding before any device check or
+    library call: each would otherwise reach the kernels as raw pointers and
+    read or write past a tensor's end.  Extra (padding) rows are allowed."""
+    import torch
+    T, N, hk, hv, K, V = 10, 2, 2, 4, 32, 64
+    bf = torch.bfloat16
+    q = torch.zeros(T, hk, K, dtype=bf)
+    v = torch.zeros(T, hv, V, dtype=bf)
+    g = torch.zeros(T, hv, K)
+    beta = torch.zeros(T, hv)
+    cu = torch.tensor([0, 4, T], dtype=torch.int32)
+    h0 = torch.zeros(N, hv, V, K)
+    pool = torch.zeros(6, hv, V, K)
+    idx = torch.zeros(N, dtype=torch.int32)
+    pf = kda.chunk_prefill
+    bad = [
+        (lambda: pf(q, q[:, :1].contiguous(), v, g, beta, cu), "k must have shape"),
+        (lambda: pf(q, q, v[:T - 1].contiguous(), g, beta, cu), "v must have shape"),
+        (lambda: pf(q, q, v[:, :3].contiguous(), g, beta, cu), "multiple of key heads"),
+        (lambda: pf(q, q, v, g[:, :, :16].contiguous(), beta, cu), "g must have shape"),
+        (lambda: pf(q, q, v, g[:T - 2].contiguous(), beta, cu), "g must have shape"),
+        (lambda: pf(q, q, v, g, beta[:T - 1].contiguous(), cu), "beta must have shape"),
+        (lambda: pf(q, q, v, g, beta, cu, initial_state=h0[:1].contiguous()), "initial_state must have shape"),
+        (lambda: pf(q, q, v, g, beta, cu, initial_state=h0.transpose(2, 3).contiguous()),
+         "initial_state must have shape"),
+        (lambda: pf(q, q, v, g, beta, cu, initial_state=pool.transpose(2, 3).contiguous(), state_indices=idx),
+         "state pool must have shape"),
+        (lambda: pf(q, q, v, g, beta, cu, initial_state=pool, state_indices=idx[:1].contiguous()),
+         "state_indices must have shape"),
+        (lambda: kda.chunk_prefill_fused_gate(q, q, v, g.to(bf), torch.zeros(hv, K), torch.zeros(hv, K),
+                                              beta[:3].to(bf).contiguous(), cu), "beta_x must have shape"),
+    ]
+    for call, msg in bad:
+        with pytest.raises(ValueError, match=msg):
+            call()
+    # padding rows past T are accepted (refused only for being host tensors)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        pf(q, torch.zeros(T + 3, hk, K, dtype=bf), torch.zeros(T + 3, hv, V, dtype=bf), torch.zeros(T + 3, hv, K),
+           torch.zeros(T + 3, hv), cu, initial_state=torch.zeros(N + 1, hv, V, K))
+    # decode
+    B = 3
+    qd, vd = q[:B].contiguous(), v[:B].contiguous()
+    gd, bd = g[:B].contiguous(), beta[:B].contiguous()
+    dec = kda.recurrent_decode
+    bad = [
+        (lambda: dec(qd, qd, vd, gd, bd, pool.transpose(2, 3).contiguous(), idx[:1].repeat(B)),
+         "state_pool must have shape"),
+        (lambda: dec(qd, qd, vd, gd, bd, pool, idx[:2].contiguous()), "state_indices must have shape"),
+        (lambda: dec(qd, qd, vd[:2].contiguous(), gd, bd, pool, idx.repeat(2)), "v must have shape"),
+        (lambda: dec(qd, qd, vd, gd[:, :2].contiguous(), bd, pool, idx.repeat(2)), "g must have shape"),
+        (lambda: kda.recurrent_decode_multi(qd, qd, vd, gd, bd, torch.tensor([0, 1, B], dtype=torch.int32),
+                                            pool, idx[:1].contiguous()), "state_indices must have shape"),
+        (lambda: kda.recurrent_decode_packed(torch.zeros(B, 2 * hk * K + hv * V, dtype=bf), gd, bd,
+                                             pool, idx[:2].contiguous(), hk=hk, hv=hv, dk=K, dv=V),
+         "state_indices must have shape"),
+    ]
+    for call, msg in bad:
+        with pytest.raises(ValueError, match=msg):
+            call()

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import kda_workloads as W
-from gpu_util import O_MAXABS, STATE_REL_F32, dev, host, max_abs, rel_l2, say
+from gpu_util import O_MAXABS, STATE_REL_F32, check_states, dev, host, max_abs, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -37,10 +37,10 @@ def run_and_check(K, oracle, inp, name):
                                    scale=inp.scale)
     og, hg = host(o), host(ht)
     assert np.isfinite(og).all() and np.isfinite(hg).all(), name
-    e_o, e_s = max_abs(og, o_ref), rel_l2(hg, ht_ref)
-    say("%s: o max-abs %.3e  state rel-L2 %.3e" % (name, e_o, e_s))
+    e_o = max_abs(og, o_ref)
+    say("%s: o max-abs %.3e" % (name, e_o))
     assert e_o <= O_MAXABS, name
-    assert e_s <= STATE_REL_F32, name
+    check_states(name, hg, ht_ref)
     return og, hg, o_ref, ht_ref
 
 
@@ -106,10 +106,10 @@ def test_large_token_count(K, oracle):
     o_ref, ht_ref = oracle.prefill(sel(inp.q), sel(inp.k), sel(inp.v), sel(inp.g), sel(inp.beta),
                                    inp.cu_seqlens, h0=sel(inp.h0), scale=inp.scale)
     assert np.isfinite(og).all() and np.isfinite(hg).all()
-    e_o, e_s = max_abs(og, o_ref), rel_l2(hg, ht_ref)
-    say("T=131072 heads %s: o max-abs %.3e  state rel-L2 %.3e" % (heads, e_o, e_s))
+    e_o = max_abs(og, o_ref)
+    say("T=131072 heads %s: o max-abs %.3e" % (heads, e_o))
     assert e_o <= O_MAXABS
-    assert e_s <= STATE_REL_F32
+    check_states("T=131072", hg, ht_ref)
 
 
 def test_mixed_device_arguments_refused(K):

@@ -61,3 +61,44 @@ def test_graph_replay_matches_eager(K):
               and torch.equal(pool, pool_e))
         say("graph replay %d: bit-identical %s (junk %.3f)" % (r, ok, float(junk)))
         assert ok, r
+
+
+def test_graph_survives_workspace_growth(K):
+    """A prefill captured on a stream keeps working after a larger eager
+    prefill on that stream has replaced the stream's workspace: the replaced
+    buffer stays alive, so a tensor allocated afterwards is not overwritten
+    by the replay, and the replay still matches the eager result."""
+    small = W.make_prefill(603, [100, 30], 2, 4, 128, 128, gate="realistic", h0="random")
+    big = W.make_prefill(604, [3000, 2000], 2, 4, 128, 128, gate="realistic", h0="random")
+    P = {n: dev(getattr(small, n)) for n in ("q", "k", "v", "g", "beta", "cu_seqlens", "h0")}
+
+    def work():
+        return K.chunk_prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu_seqlens"],
+                               initial_state=P["h0"])
+
+    o_e, ht_e = (x.clone() for x in work())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()                                          # the stream's first (small) workspace
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        o_g, ht_g = work()
+    torch.cuda.synchronize()
+    old_bytes = K._WS[(torch.cuda.current_device(), s.cuda_stream)].numel()
+    with torch.cuda.stream(s):                          # grows the stream's workspace
+        K.chunk_prefill(*(dev(getattr(big, n)) for n in ("q", "k", "v", "g", "beta", "cu_seqlens")),
+                        initial_state=dev(big.h0))
+    torch.cuda.synchronize()
+    assert K._WS[(torch.cuda.current_device(), s.cuda_stream)].numel() > old_bytes
+    # tensors the size of the replaced workspace: the allocator would hand
+    # them its memory first if it had been freed
+    sentinels = [torch.full((old_bytes // 4,), 7.0, device="cuda") for _ in range(4)]
+    for r in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        ok = torch.equal(o_g, o_e) and torch.equal(ht_g, ht_e)
+        clean = all(bool((t == 7.0).all()) for t in sentinels)
+        say("graph replay %d after workspace growth: bit-identical %s, sentinels intact %s" % (r, ok, clean))
+        assert ok and clean, r

@@ -5,7 +5,8 @@ import pytest
 import torch
 
 import kda_workloads as W
-from gpu_util import (O_MAXABS, STATE_REL_BF16, STATE_REL_F32, dev, host, max_abs, rel_l2, say)
+from gpu_util import (O_MAXABS, STATE_REL_BF16, STATE_REL_F32, check_states, dev, host, max_abs, rel_l2,
+                      say)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,16 +28,15 @@ def run_dense(K, inp, h0=None, state_dtype=None):
 
 
 def check(name, o, ht, o_ref, ht_ref, state_bf16=False):
+    """o max-abs against the oracle; final states by whole-tensor and
+    worst-(sequence, head) relative L2."""
     og, hg = host(o), host(ht)
     assert np.isfinite(og).all() and np.isfinite(hg).all()
     e_o = max_abs(og, o_ref)
-    e_s = rel_l2(hg, ht_ref)
-    worst = max((rel_l2(hg[n, h], ht_ref[n, h]) for n in range(ht_ref.shape[0])
-                 for h in range(ht_ref.shape[1]) if np.linalg.norm(ht_ref[n, h]) > 0), default=0.0)
-    say("%s: o max-abs %.3e (|o| max %.2f)  state rel-L2 %.3e (worst unit %.3e)"
-        % (name, e_o, float(np.abs(o_ref).max()) if o_ref.size else 0.0, e_s, worst))
+    say("%s: o max-abs %.3e (|o| max %.2f)"
+        % (name, e_o, float(np.abs(o_ref).max()) if o_ref.size else 0.0))
     assert e_o <= O_MAXABS, name
-    assert e_s <= (STATE_REL_BF16 if state_bf16 else STATE_REL_F32), name
+    check_states(name, hg, ht_ref, bf16=state_bf16)
 
 
 def test_single_sequence_fp32(K, oracle):
@@ -83,19 +83,26 @@ def test_pool_matches_dense_bitwise(K, oracle, state_dtype):
 def test_kimi_shaped_realistic_gates_full(K, oracle):
     """The bench workload: 16 sequences of 512..4096 tokens, Hk = Hv = 32,
     K = V = 128, realistic gates (in-chunk cumulative log-decay up to ~1e4),
-    fp32 pool of 32 slots.  Every output and every written row is compared."""
+    fp32 pool of 32 slots.  Every output and every written row is compared
+    with the oracle, and the pool-mode call with a dense-mode twin bit for
+    bit (512 chains: the state kernel's sixteen-wave form)."""
     say("generating prefill workload (16 seqs, 512..4096 tokens, 32 heads)")
     inp = W.kimi_prefill_16seq()
     S = inp.pool.shape[0]
     slots = oracle.map_slot(inp.indices.numpy(), S)
+    sl = torch.as_tensor(slots)
     pool_before = inp.pool.clone()
     pool = dev(inp.pool)
     o, _ = K.chunk_prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
                            dev(inp.cu_seqlens), initial_state=pool, state_indices=dev(inp.indices))
     torch.cuda.synchronize()
+    o_d, ht_d = run_dense(K, inp, h0=pool_before[sl])
+    assert torch.equal(o, o_d)
+    assert torch.equal(pool[sl.cuda()], ht_d)
+    del o_d, ht_d
     o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens,
-                                   h0=pool_before[torch.as_tensor(slots)])
-    check("kimi_prefill_16seq", o, pool[torch.as_tensor(slots).cuda()], o_ref, ht_ref)
+                                   h0=pool_before[sl])
+    check("kimi_prefill_16seq", o, pool[sl.cuda()], o_ref, ht_ref)
     untouched = np.setdiff1d(np.arange(S), slots)
     assert torch.equal(pool[torch.as_tensor(untouched).cuda()].cpu(), pool_before[torch.as_tensor(untouched)])
 
@@ -190,3 +197,46 @@ def test_deterministic(K):
     a = run_dense(K, inp)
     b = run_dense(K, inp)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_dense_in_place(K, oracle):
+    """Dense mode with final_state == initial_state (the in-place form the
+    header allows): the final states overwrite the initial ones."""
+    import ctypes
+    inp = W.make_prefill(69, [150, 7, 64], 2, 4, 128, 128, gate="realistic", h0="random")
+    q, k, v, g, beta, cu = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens))
+    h = dev(inp.h0)
+    T, hv, dv = v.shape
+    o = torch.empty(T, hv, dv, dtype=q.dtype, device="cuda")
+    desc = K.prefill_desc(q, v, g, 3, torch.float32, 1.0)
+    ws = torch.empty(K.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    st = K.lib().kda_chunk_prefill(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                   beta.data_ptr(), cu.data_ptr(), h.data_ptr(), None, h.data_ptr(),
+                                   o.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=inp.h0)
+    check("dense in place", o, h, o_ref, ht_ref)
+    o2, ht2 = run_dense(K, inp)   # out of place: bitwise the same
+    assert torch.equal(o, o2) and torch.equal(h, ht2)
+
+
+@pytest.mark.parametrize("s", [64.0, 1.0 / 64.0, 1000.0])
+def test_value_and_state_magnitudes(K, oracle, s):
+    """The prefill's matrix-core operands are fp16: relative errors do not
+    depend on the magnitude of v and the states while it stays inside fp16's
+    normal range (2^-14 .. 65504).  v and h0 scaled by s: the same state
+    bounds, o max-abs bound scaled by s."""
+    inp = W.varlen_gqa5()
+    inp.v = (inp.v.float() * s).to(inp.v.dtype)
+    inp.h0 = inp.h0 * s
+    o, ht = run_dense(K, inp)
+    o_ref, ht_ref = oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, h0=inp.h0)
+    og = host(o)
+    assert np.isfinite(og).all()
+    e_o = max_abs(og, o_ref)
+    say("v, h0 x %g: o max-abs %.3e (bound %.3e), |state| max %.1f" % (s, e_o, O_MAXABS * s,
+                                                                      float(np.abs(ht_ref).max())))
+    assert e_o <= O_MAXABS * s
+    check_states("v, h0 x %g" % s, host(ht), ht_ref)
