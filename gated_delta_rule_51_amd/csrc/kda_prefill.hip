@@ -867,10 +867,12 @@ __global__ __launch_bounds__(NTI, 4) void intra_kernel(PrefillArgs a, Work w) {
 // Each operand register is reloaded with the next chunk's tile right after
 // its last use, so its load has a whole chunk step to arrive with a single
 // register copy; the register budget (<= 128 VGPRs) then admits sixteen
-// waves per CU: one chain of 128 value columns, or two of at most 64.
+// waves per CU: one chain of 128 value columns, or two of at most 64.  With
+// at most 64 chains a chain's 128 columns are split into four parts of 32.
 // ---------------------------------------------------------------------------
 constexpr int NTS = 512;   // threads of the state kernel per column part
 constexpr long kFewChains = 256;   // at most this many chains: one workgroup per column part
+constexpr long kVeryFewChains = 64;   // at most this many: four parts of 32 value columns
 
 template <int DK, int DV, typename IO> struct StateSmem {
     _Float16 Sh[DV][DK + PADH];   // S^T as fp16 (B operand of W S and Q exp(G) S)
@@ -1283,7 +1285,15 @@ hipError_t launch_state_st(PrefillArgs &a, Work &w, hipStream_t s) {
     constexpr int NPART = DV / DVW;
     static_assert(NPART == (DV == 128 ? 2 : 1), "column parts");
     if constexpr (NPART > 1) {
-        if ((long)a.hv * a.num_seqs <= kFewChains) return launch_state_w<DK, DV, DVW, 1, IO, ST>(a, w, s);
+        // With few chains the chain step's latency, not the operand stream,
+        // sets the time: shorter dependent MFMA chains per part pay for the
+        // extra (cache-served) operand reads.  Measured on MI355X, one
+        // workgroup per part: 1 x 32768 tokens x 32 heads 1.415 ms with two
+        // parts, 1.28 ms with four; 1 x 4096 x 1 0.135 -> 0.108 ms; at 128
+        // chains and more two parts are faster.
+        const long chains = (long)a.hv * a.num_seqs;
+        if (chains <= kVeryFewChains) return launch_state_w<DK, DV, 32, 1, IO, ST>(a, w, s);
+        if (chains <= kFewChains) return launch_state_w<DK, DV, DVW, 1, IO, ST>(a, w, s);
     }
     return launch_state_w<DK, DV, DVW, NPART, IO, ST>(a, w, s);
 }
