@@ -35,6 +35,8 @@ METRIC = "KDA prefill tokens/s + MFMA util; decode states/s + HBM GB/s vs peak"
 DECODE_KERNEL = "kda::decode_kernel<128, 128, kda::bf16, float, false, false, true>"
 DECODE_SRC = os.path.join(ROOT, "gated_delta_rule_51_amd", "csrc", "kda_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b4096_traffic.json")
+PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_51_amd", "csrc", "kda_prefill.hip")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_16seq_traffic.json")
 
 
 def _sha(path):
@@ -43,18 +45,18 @@ def _sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs recorded under profiles/ (scaled by a plain copy of known size), or
-    None when the decode source changed since the counters were taken."""
+def measured_traffic(path=TRAFFIC_FILE, src=DECODE_SRC):
+    """The rocprofv3 FETCH_SIZE / WRITE_SIZE record under profiles/ (HBM bytes
+    per launch, scaled by a plain copy of known size), or None when the
+    kernel source changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != _sha(DECODE_SRC):
+    if rec.get("kernel_source_sha256_16") != _sha(src):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
 
 
 def prefill_work(cu, hk, hv, dk, dv, chunk=64, gate_bytes=4):
@@ -326,10 +328,18 @@ def main():
 
     # dominant kernel: the decode kernel (one launch per step, timed by the
     # events that bracket it on the stream it runs on)
+    if do_pre:
+        ptr = measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRC)
+        # counted HBM bytes of one prefill call (meta, intra and state kernels)
+        # and their ratio to the algorithmic bytes
+        prefill["traffic"] = ptr.get("traffic_bytes_per_call") if ptr else None
+        prefill["traffic_over_alg"] = prefill["traffic"] / pb if prefill["traffic"] else None
     if do_dec:
+        dtr = measured_traffic()
         roof = {"kernel": DECODE_KERNEL, "bound": "hbm",
                 "achieved": decode["alg_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": decode["alg_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                "frac": decode["alg_gbs"] / HBM_PEAK_GBS,
+                "traffic": dtr.get("traffic_bytes_per_launch") if dtr else None,
                 "alg_bytes_per_launch": db}
     else:
         roof = {"kernel": "prefill (meta + intra + state)", "bound": "hbm",
