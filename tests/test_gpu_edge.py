@@ -124,3 +124,44 @@ def test_mixed_device_arguments_refused(K):
             K.chunk_prefill(*bad)
     with pytest.raises(ValueError, match="must be on"):
         K.chunk_prefill(*args, initial_state=dev(inp.h0).cpu())
+
+
+def test_decode_equals_one_token_prefill(K, oracle):
+    """A one-token decode of B requests equals a prefill of B one-token
+    sequences from the same states (within the prefill's tolerances: the
+    prefill's matrix-core operands are fp16, the decode is fp32); both are
+    held to the oracle too."""
+    d = W.make_decode(78, 24, 2, 4, 128, 128, num_slots=30)
+    S = d.pool.shape[0]
+    slots = oracle.map_slot(d.indices.numpy(), S)
+    pool = dev(d.pool)
+    od = K.recurrent_decode(dev(d.q), dev(d.k), dev(d.v), dev(d.g), dev(d.beta), pool, dev(d.indices))
+    cu = torch.arange(0, 25, dtype=torch.int32)
+    op, hp = K.chunk_prefill(dev(d.q), dev(d.k), dev(d.v), dev(d.g), dev(d.beta), dev(cu),
+                             initial_state=dev(d.pool[torch.as_tensor(slots)]))
+    torch.cuda.synchronize()
+    hd = host(pool[torch.as_tensor(slots).cuda()])
+    e_o, e_s = max_abs(host(od), host(op)), rel_l2(host(hp), hd)
+    say("decode vs one-token prefill: o max-abs %.3e  state rel-L2 %.3e" % (e_o, e_s))
+    assert e_o <= O_MAXABS and e_s <= STATE_REL_F32
+    o_ref, ht_ref = oracle.decode(d.q, d.k, d.v, d.g, d.beta, d.pool[torch.as_tensor(slots)])
+    assert max_abs(host(od), o_ref) <= O_MAXABS and max_abs(host(op), o_ref) <= O_MAXABS
+    check_states("decode", hd, ht_ref)
+    check_states("one-token prefill", host(hp), ht_ref)
+
+
+def test_empty_calls(K):
+    """N = 0 sequences (prefill) and B = 0 requests (decode) are accepted and
+    launch nothing; the outputs are empty."""
+    q = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(0, 4, 64, dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros(0, 4, 64, device="cuda")
+    beta = torch.zeros(0, 4, device="cuda")
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o, ht = K.chunk_prefill(q, q, v, g, beta, cu)
+    pool = torch.randn(3, 4, 64, 64, device="cuda")
+    before = pool.clone()
+    od = K.recurrent_decode(q, q, v, g, beta, pool, torch.zeros(0, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert o.shape == (0, 4, 64) and ht.shape == (0, 4, 64, 64) and od.shape == (0, 4, 64)
+    assert torch.equal(pool, before)
