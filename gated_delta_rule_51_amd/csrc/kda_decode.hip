@@ -34,16 +34,36 @@ template <int DK, int BV, typename ST> struct RowTile {
     static_assert(DK % VEC == 0 && LPR <= 64, "tile");
 };
 
-// Load this thread's part of the BV rows at `st` (row stride DK) into s.
+// Element offsets of this thread's rows within a block of BV stored rows.
+// With OPAQUE they are formed once and hidden from the compiler, which
+// otherwise re-forms the row addresses between the row stores at the end of
+// the one-token decode; the stores then go out back to back (measured 3.7%
+// faster for the B = 4096 decode).
+template <int DK, int BV, typename ST, bool OPAQUE = false>
+__device__ __forceinline__ void row_offs(int r0, int cg, unsigned (&ro)[RowTile<DK, BV, ST>::NP]) {
+    using R = RowTile<DK, BV, ST>;
+#pragma unroll
+    for (int p = 0; p < R::NP; ++p) {
+        ro[p] = (unsigned)((r0 + p * R::RPP) * DK + cg * R::VEC);
+        if constexpr (OPAQUE) asm volatile("" : "+v"(ro[p]));
+    }
+}
+
+// Whether pass p holds a row of the block (always, when the passes tile it).
+template <int DK, int BV, typename ST> __device__ __forceinline__ bool row_in(int r0, int p) {
+    using R = RowTile<DK, BV, ST>;
+    return R::NP * R::RPP == BV || r0 + p * R::RPP < BV;
+}
+
+// Load this thread's part of the rows at st (offsets ro) into s.
 template <int DK, int BV, typename ST, bool NT>
-__device__ __forceinline__ void load_rows(const ST *st, int r0, int cg,
+__device__ __forceinline__ void load_rows(const ST *st, const unsigned (&ro)[RowTile<DK, BV, ST>::NP], int r0,
                                           float (&s)[RowTile<DK, BV, ST>::NP][RowTile<DK, BV, ST>::VEC]) {
     using R = RowTile<DK, BV, ST>;
 #pragma unroll
     for (int p = 0; p < R::NP; ++p) {
-        const int row = r0 + p * R::RPP;
-        if (row < BV) {
-            const ST *src = st + (long)row * DK + cg * R::VEC;
+        if (row_in<DK, BV, ST>(r0, p)) {
+            const ST *src = st + ro[p];
             if constexpr (R::VEC == 4) {
                 f32x4 x = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src)) : load4(src);
 #pragma unroll
@@ -61,16 +81,16 @@ __device__ __forceinline__ void load_rows(const ST *st, int r0, int cg,
     }
 }
 
-// Store this thread's part of the rows to `st` (bf16 storage rounds to nearest even).
+// Store this thread's part of the rows to st (offsets ro; bf16 storage rounds
+// to nearest even).
 template <int DK, int BV, typename ST, bool NT>
-__device__ __forceinline__ void store_rows(ST *st, int r0, int cg,
+__device__ __forceinline__ void store_rows(ST *st, const unsigned (&ro)[RowTile<DK, BV, ST>::NP], int r0,
                                            const float (&s)[RowTile<DK, BV, ST>::NP][RowTile<DK, BV, ST>::VEC]) {
     using R = RowTile<DK, BV, ST>;
 #pragma unroll
     for (int p = 0; p < R::NP; ++p) {
-        const int row = r0 + p * R::RPP;
-        if (row < BV) {
-            ST *dst = st + (long)row * DK + cg * R::VEC;
+        if (row_in<DK, BV, ST>(r0, p)) {
+            ST *dst = st + ro[p];
             if constexpr (R::VEC == 4) {
                 f32x4 x;
 #pragma unroll
@@ -143,9 +163,10 @@ __device__ __forceinline__ void token_inputs(const DecodeArgs &a, long t, int h,
 }
 
 // One token applied to this thread's rows: decay, residual against v, rank-1
-// write, read-out; lane cg == 0 of each row writes o.
-template <int DK, int BV, typename IO, typename ST>
-__device__ __forceinline__ void token_update(const IO *vp, IO *op, float scale, int r0, int cg,
+// write, read-out; lane cg == 0 of each row writes o.  vrow(p, row) gives the
+// token's v value of the thread's row p (stored row `row`).
+template <int DK, int BV, typename IO, typename ST, typename VF>
+__device__ __forceinline__ void token_update(VF vrow, IO *op, float scale, int r0, int cg,
                                              float (&s)[RowTile<DK, BV, ST>::NP][RowTile<DK, BV, ST>::VEC],
                                              const float (&kk)[RowTile<DK, BV, ST>::VEC],
                                              const float (&qq)[RowTile<DK, BV, ST>::VEC],
@@ -154,7 +175,7 @@ __device__ __forceinline__ void token_update(const IO *vp, IO *op, float scale, 
 #pragma unroll
     for (int p = 0; p < R::NP; ++p) {
         const int row = r0 + p * R::RPP;
-        if (row < BV) {
+        if (row_in<DK, BV, ST>(r0, p)) {
             float pk = 0.f;
 #pragma unroll
             for (int i = 0; i < R::VEC; ++i) {
@@ -162,7 +183,7 @@ __device__ __forceinline__ void token_update(const IO *vp, IO *op, float scale, 
                 pk += s[p][i] * kk[i];
             }
             pk = group_sum<R::LPR>(pk);
-            const float u = beta * (io_traits<IO>::load(vp, row) - pk);
+            const float u = beta * (vrow(p, row) - pk);
             float pq = 0.f;
 #pragma unroll
             for (int i = 0; i < R::VEC; ++i) {
@@ -194,16 +215,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     ST *st = reinterpret_cast<ST *>(a.state) + (((long)slot * a.hv + h) * a.dv + j0) * (long)DK;
 
     // Issue every state load first.
+    unsigned ro[R::NP];
+    row_offs<DK, BV, ST, true>(r0, cg, ro);
     float s[R::NP][R::VEC];
-    load_rows<DK, BV, ST, NT>(st, r0, cg, s);
+    load_rows<DK, BV, ST, NT>(st, ro, r0, s);
 
     float dec[R::VEC], kk[R::VEC], qq[R::VEC], beta;
     token_inputs<DK, R::VEC, IO, SCALAR, RAW>(a, b, h, hk_idx, cg * R::VEC, kk, qq, dec, beta);
     const IO *vp = reinterpret_cast<const IO *>(a.v) + (long)b * a.v_stride + (long)h * a.dv + j0;
     IO *op = reinterpret_cast<IO *>(a.o) + ((long)b * a.hv + h) * a.dv + j0;
-    token_update<DK, BV, IO, ST>(vp, op, a.scale, r0, cg, s, kk, qq, dec, beta);
+    token_update<DK, BV, IO, ST>([&](int, int row) { return io_traits<IO>::load(vp, row); }, op, a.scale,
+                                 r0, cg, s, kk, qq, dec, beta);
 
-    store_rows<DK, BV, ST, NT>(st, r0, cg, s);
+    store_rows<DK, BV, ST, NT>(st, ro, r0, s);
 }
 
 // Multi-token decode: request b runs its tokens [cu[b], cu[b+1]) one after
@@ -231,8 +255,10 @@ __global__ __launch_bounds__(256) void multi_decode_kernel(DecodeArgs a) {
     int slot = a.indices[b];
     if (slot < 0) slot = a.num_slots - 1;
     ST *st = reinterpret_cast<ST *>(a.state) + (((long)slot * a.hv + h) * a.dv + j0) * (long)DK;
+    unsigned ro[R::NP];
+    row_offs<DK, BV, ST>(r0, cg, ro);
     float s[R::NP][R::VEC];
-    load_rows<DK, BV, ST, true>(st, r0, cg, s);
+    load_rows<DK, BV, ST, true>(st, ro, r0, s);
 
     const long step_elems = (long)a.hv * a.dv * DK;   // one cached step of one request
     ST *cache = reinterpret_cast<ST *>(a.cache);
@@ -244,16 +270,25 @@ __global__ __launch_bounds__(256) void multi_decode_kernel(DecodeArgs a) {
         token_inputs<DK, R::VEC, IO, SCALAR, RAW>(a, min(t + 1, t1 - 1), h, hk_idx, cg * R::VEC, kk2, qq2, dec2, beta2);
         const IO *vp = reinterpret_cast<const IO *>(a.v) + (long)t * a.v_stride + (long)h * a.dv + j0;
         IO *op = reinterpret_cast<IO *>(a.o) + ((long)t * a.hv + h) * a.dv + j0;
-        token_update<DK, BV, IO, ST>(vp, op, a.scale, r0, cg, s, kk, qq, dec, beta);
+        token_update<DK, BV, IO, ST>([&](int, int row) { return io_traits<IO>::load(vp, row); }, op, a.scale,
+                                     r0, cg, s, kk, qq, dec, beta);
         const int j = t - t0;
         if (cache != nullptr && j < a.cache_pitch)
             store_rows<DK, BV, ST, true>(cache + ((long)b * a.cache_pitch + j) * step_elems +
-                                             ((long)h * a.dv + j0) * DK, r0, cg, s);
+                                             ((long)h * a.dv + j0) * DK, ro, r0, s);
 #pragma unroll
         for (int i = 0; i < R::VEC; ++i) { dec[i] = dec2[i]; kk[i] = kk2[i]; qq[i] = qq2[i]; }
         beta = beta2;
     }
-    if (a.update_pool) store_rows<DK, BV, ST, true>(st, r0, cg, s);
+    if (a.update_pool) {
+        // the row offsets re-formed here, so that those of the initial load
+        // are not kept live through the token loop
+        int r0x = r0, cgx = cg;
+        asm volatile("" : "+v"(r0x), "+v"(cgx));
+        unsigned rx[R::NP];
+        row_offs<DK, BV, ST>(r0x, cgx, rx);
+        store_rows<DK, BV, ST, true>(st, rx, r0x, s);
+    }
 }
 
 template <int DK, int BV, typename IO, typename ST, bool SCALAR>

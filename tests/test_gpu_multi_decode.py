@@ -137,6 +137,16 @@ def test_multi_view_of_larger_cache(K, oracle):
     check(K, oracle, m, "multi view pitch 8", alloc_steps=8)
 
 
+@pytest.mark.parametrize("fused,state", [(False, "f32"), (True, "bf16")])
+def test_multi_long_requests(K, oracle, fused, state):
+    """Requests longer than the kernel's batch of tokens staged in LDS (8):
+    9, 17 and 12 tokens run in two or three batches; steps at or beyond the
+    pitch of 10 are not cached."""
+    m = W.make_multi_decode(410, [9, 17, 3, 8, 12, 1], 2, 4, 128, 128, num_slots=8, cache_pitch=10,
+                            state_dtype=state)
+    check(K, oracle, m, "multi long requests%s %s" % (" fused" if fused else "", state), fused=fused)
+
+
 def test_multi_read_only_pool(K, oracle):
     m = W.make_multi_decode(404, [4, 4, 4], 2, 4, 128, 128, num_slots=5, cache_pitch=4)
     check(K, oracle, m, "multi read-only pool", update_pool=False)
