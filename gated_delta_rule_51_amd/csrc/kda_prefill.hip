@@ -899,14 +899,14 @@ __device__ __forceinline__ void store_state4(bf16 *p, const f32x4 &v) {
 // no swizzle; untyped 16-byte accesses with a byte range check.
 constexpr int kBufferWord3 = 0x00020000;
 
-// A wave-uniform element offset made opaque (both halves through
-// readfirstlane).  Added to a kernel-argument pointer it keeps the global
-// address space, and the compiler cannot fold per-lane offsets into a
-// loop-invariant 64-bit per-lane pointer per operand stream.
 // Keeps the loads issued before it from being sunk past it by the compiler
 // (a prefetch sunk to its use would expose the full memory latency).
 __device__ __forceinline__ void pin_loads() { asm volatile("" ::: "memory"); }
 
+// A wave-uniform element offset made opaque (both halves through
+// readfirstlane).  Added to a kernel-argument pointer it keeps the global
+// address space, and the compiler cannot fold per-lane offsets into a
+// loop-invariant 64-bit per-lane pointer per operand stream.
 __device__ __forceinline__ size_t uniform_off(size_t x) {
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
     const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
