@@ -112,8 +112,8 @@ kda_status prefill_impl(const kda_prefill_desc *d, const void *q, const void *k,
     if (T == 0 && !final_state) return KDA_OK;
 
     // Grids, all 1-D: intra over (chunk slot, head) items; state over
-    // (sequence, head) pairs (at most 256 of them: two column-part
-    // workgroups each, a few hundred in all).
+    // (sequence, head) chains, one workgroup per chain, or with at most 256
+    // chains one per column part (two, or four with at most 64 chains).
     int dev = 0, max_x = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess)
