@@ -9,7 +9,10 @@
 * the same recipe through the fused-gate entry point (raw a and b);
 * more than 256 (sequence, head) chains, where the state kernel runs both
   column parts of a chain in one sixteen-wave workgroup, with a bf16 pool and
-  with fp32 io.
+  with fp32 io;
+* 65 to 256 chains, where each column part is a workgroup of its own, with
+  the same two variants (the four-part form for at most 64 chains is covered
+  by the five-sequence recipes above).
 
 Each pool-mode result is also held to the oracle's tolerances.
 """
@@ -102,3 +105,12 @@ def test_many_chains_fp32_io(K, oracle):
     inp = W.make_prefill(82, (40, 1, 300), 4, 8, 128, 128, io="f32", gate="realistic", pool_slots=48,
                          pad_one=True, scale=128 ** -0.5)
     pool_vs_dense(K, oracle, inp, "320 chains, fp32 io")
+
+
+@pytest.mark.parametrize("io,state", [("bf16", "bf16"), ("f32", "f32")])
+def test_mid_chain_count_forms(K, oracle, io, state):
+    """20 sequences x 8 heads = 160 chains with V = 128: one state workgroup
+    per 64-column part; bf16 io with a bf16 pool, fp32 io with an fp32 pool."""
+    inp = W.make_prefill(83, (20, 1, 300), 4, 8, 128, 128, io=io, gate="realistic", pool_slots=24,
+                         state_dtype=state, pad_one=True, scale=128 ** -0.5)
+    pool_vs_dense(K, oracle, inp, "160 chains, %s io, %s pool" % (io, state))
