@@ -9,8 +9,8 @@ moderate or realistic decays, activated on the host or from raw inputs in
 the kernels), and dense or pool mode (with a -1 index).  The prefill's final
 states then seed a decode step of the same heads.  Every output is compared
 with the oracle at the suite's tolerances; pool rows that are not indexed
-must stay bit-identical.  The drawn configuration is printed before the
-GPU calls.
+must stay bit-identical.  Further cases draw multi-token (verify) decodes.
+The drawn configuration is printed before the GPU calls.
 """
 import numpy as np
 import pytest
@@ -136,3 +136,42 @@ def test_random_configuration(K, oracle, case):
     say("case %d: %s" % (case, c))
     states = prefill_case(K, oracle, case, c)
     decode_case(K, oracle, case, c, states)
+
+
+N_VERIFY = 12
+
+
+def draw_verify(case):
+    rng = np.random.default_rng(9000 + case)
+    c = {}
+    c["dk"] = int(rng.choice([32, 64, 128]))
+    c["dv"] = int(rng.choice([32, 64, 128]))
+    c["hk"] = int(rng.choice([1, 2, 4]))
+    c["hv"] = c["hk"] * int(rng.choice([1, 2]))
+    n = int(rng.integers(1, 9))
+    c["lens"] = [int(rng.integers(0, 11)) for _ in range(n)]
+    c["pitch"] = int(rng.integers(1, 9))
+    c["io"] = str(rng.choice(["bf16", "f32"]))
+    c["state"] = str(rng.choice(["f32", "bf16"]))
+    c["scalar"] = bool(rng.random() < 0.3)
+    c["fused"] = bool(rng.random() < 0.4)
+    c["update_pool"] = bool(rng.random() < 0.6)
+    c["pad"] = int(n > 1 and rng.random() < 0.5)
+    return c
+
+
+@pytest.mark.parametrize("case", range(N_VERIFY))
+def test_random_verify_configuration(K, oracle, case):
+    """Multi-token (verify) decode: requests of 0 to 10 tokens, a random
+    cache pitch (steps at or beyond it are not cached), read-only or updated
+    pool, an optional -1 index; checked by the verify suite's comparison
+    (every token's o, every cached step, the pool row, and every cache entry
+    and pool row the call must not write)."""
+    from test_gpu_multi_decode import check as check_multi
+    c = draw_verify(case)
+    say("verify case %d: %s" % (case, c))
+    m = W.make_multi_decode(9000 + case, c["lens"], c["hk"], c["hv"], c["dk"], c["dv"],
+                            num_slots=len(c["lens"]) + 3, cache_pitch=c["pitch"], io=c["io"],
+                            scalar_gate=c["scalar"], state_dtype=c["state"], pad=c["pad"],
+                            scale=c["dk"] ** -0.5)
+    check_multi(K, oracle, m, "verify case %d" % case, fused=c["fused"], update_pool=c["update_pool"])
