@@ -108,6 +108,30 @@ __device__ __forceinline__ void store_rows(ST *st, const unsigned (&ro)[RowTile<
     }
 }
 
+// Store this thread's part of the rows through a buffer resource covering the
+// row block: the lane's offset is one register and each pass adds a scalar
+// offset, so the stores need no address arithmetic between them and go out
+// back to back; the range check bounds them to the block.
+template <int DK, int BV, typename ST>
+__device__ __forceinline__ void store_rows_buf(const __amdgpu_buffer_rsrc_t rsrc, unsigned voff, int r0,
+                                               const float (&s)[RowTile<DK, BV, ST>::NP][RowTile<DK, BV, ST>::VEC]) {
+    using R = RowTile<DK, BV, ST>;
+#pragma unroll
+    for (int p = 0; p < R::NP; ++p) {
+        if (row_in<DK, BV, ST>(r0, p)) {
+            u32x4 w;
+            if constexpr (R::VEC == 4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(s[p][i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(s[p][2 * i], s[p][2 * i + 1]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(w, rsrc, voff, p * R::RPP * DK * (int)sizeof(ST), 2);
+        }
+    }
+}
+
 // The per-token inputs of one (token t, value head h) for channels c0 .. c0+VEC-1:
 // k, q, the decay factors exp(g) and beta (activated here from raw inputs if RAW).
 template <int DK, int VEC, typename IO, bool SCALAR, bool RAW>
@@ -273,9 +297,12 @@ __global__ __launch_bounds__(256) void multi_decode_kernel(DecodeArgs a) {
         token_update<DK, BV, IO, ST>([&](int, int row) { return io_traits<IO>::load(vp, row); }, op, a.scale,
                                      r0, cg, s, kk, qq, dec, beta);
         const int j = t - t0;
-        if (cache != nullptr && j < a.cache_pitch)
-            store_rows<DK, BV, ST, true>(cache + ((long)b * a.cache_pitch + j) * step_elems +
-                                             ((long)h * a.dv + j0) * DK, ro, r0, s);
+        if (cache != nullptr && j < a.cache_pitch) {
+            ST *cb = cache + ((long)b * a.cache_pitch + j) * step_elems + ((long)h * a.dv + j0) * DK;
+            const __amdgpu_buffer_rsrc_t cr =
+                __builtin_amdgcn_make_buffer_rsrc(cb, 0, BV * DK * (int)sizeof(ST), kBufferWord3);
+            store_rows_buf<DK, BV, ST>(cr, ro[0] * (unsigned)sizeof(ST), r0, s);
+        }
 #pragma unroll
         for (int i = 0; i < R::VEC; ++i) { dec[i] = dec2[i]; kk[i] = kk2[i]; qq[i] = qq2[i]; }
         beta = beta2;

@@ -50,6 +50,10 @@ __device__ __forceinline__ float sigmoid_f(float b) {
     return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-b * kLog2e));
 }
 
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle; untyped 16-byte accesses with a byte range check.
+constexpr int kBufferWord3 = 0x00020000;
+
 // Element type traits for io / state tensors.
 template <typename T> struct io_traits;
 template <> struct io_traits<float> {

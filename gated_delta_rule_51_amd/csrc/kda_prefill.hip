@@ -895,10 +895,6 @@ __device__ __forceinline__ void store_state4(bf16 *p, const f32x4 &v) {
 }
 
 
-// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
-// no swizzle; untyped 16-byte accesses with a byte range check.
-constexpr int kBufferWord3 = 0x00020000;
-
 // Keeps the loads issued before it from being sunk past it by the compiler
 // (a prefetch sunk to its use would expose the full memory latency).
 __device__ __forceinline__ void pin_loads() { asm volatile("" ::: "memory"); }
