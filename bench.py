@@ -15,7 +15,7 @@ the kernels) and reported under "fused_gate", and a multi-token verify decode
 (1024 requests x 4 tokens with a per-step state cache) is timed and reported
 under "spec_decode".  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -162,7 +162,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--spec-steps", type=int, default=10,
                     help="after the timed steps, time this many multi-token verify decodes "
