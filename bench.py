@@ -16,6 +16,9 @@ the kernels) and reported under "fused_gate", and a multi-token verify decode
 under "spec_decode".  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
+
+The traffic records under profiles/ (HBM bytes counted by rocprofv3) are
+written by ``--traffic-record``, from counter runs of this script.
 """
 from __future__ import annotations
 
@@ -146,6 +149,109 @@ def cpu_baseline(pre, dec, reps=5, nreq=1024):
     }
 
 
+# Kernels whose counters the traffic records hold (names as rocprofv3 prints them).
+FUSED_DECODE_KERNEL = "kda::decode_kernel<128, 128, kda::bf16, float, false, true, true>"
+MULTI_DECODE_KERNEL = "kda::multi_decode_kernel<128, 128, kda::bf16, float, false, true>"
+# (The prefill kernels sit in an unnamed namespace inside kda::.)
+PREFILL_KERNELS = (("intra", "intra_kernel<128, 128, kda::bf16, false, false>"),
+                   ("intra_fused_gate", "intra_kernel<128, 128, kda::bf16, false, true>"),
+                   ("state", "state_kernel<128, 128, 64, 2, kda::bf16, float>"),
+                   ("meta", "meta_kernel"))
+
+
+def _pmc_values(d, counter):
+    """{kernel name: [value per dispatch]} of one counter from the
+    counter_collection.csv files of a rocprofv3 --pmc output directory."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    if not out:
+        raise SystemExit("no %s values under %s" % (counter, d))
+    return out
+
+
+def _mean_of(vals, name):
+    """Mean over the dispatches of the one kernel whose name contains name."""
+    hits = [v for k, v in vals.items() if name in k]
+    if len(hits) != 1:
+        raise SystemExit("%d kernels named %s" % (len(hits), name))
+    return sum(hits[0]) / len(hits[0]), len(hits[0])
+
+
+def traffic_record(part, fetch_dir, write_dir, path=None):
+    """Write profiles/<part> traffic JSON from two rocprofv3 --pmc runs of
+    this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch) made with
+    --copy-calibration-gib 4: both counters are scaled by what they read for
+    that plain 4 GiB copy, and the record carries the hash of the kernel
+    source, so that the bench reports it only while the source is unchanged."""
+    F, Wr = _pmc_values(fetch_dir, "FETCH_SIZE"), _pmc_values(write_dir, "WRITE_SIZE")
+    cf = max(v for k, vs in F.items() if "copyBuffer" in k for v in vs)
+    cw = max(v for k, vs in Wr.items() if "copyBuffer" in k for v in vs)
+    ref_kib = 4 * 1024 * 1024
+    fs, ws = ref_kib / cf, ref_kib / cw
+    rec_cmd = ("python3 bench.py --traffic-record %s --fetch-dir <out FETCH_SIZE> --write-dir <out WRITE_SIZE>"
+               % part)
+    cmds = ["cd /tmp && rocprofv3 --pmc %s --output-format csv -d <out %s> -o run -- python3 <repo>/bench.py "
+            "--part %s --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration-gib 4 --fused-gate-steps 2 "
+            "--spec-steps 2" % (c, c, part) for c in ("FETCH_SIZE", "WRITE_SIZE")] + [rec_cmd]
+    common = {"copy_reference": "one 4 GiB device-to-device copy (rocclr copyBuffer) in the same process",
+              "copy_fetch_size_kib": cf, "copy_write_size_kib": cw, "fetch_scale": fs, "write_scale": ws}
+    both = lambda f, w: (f * fs + w * ws) * 1024
+    if part == "decode":
+        f, _ = _mean_of(F, DECODE_KERNEL)
+        w, _ = _mean_of(Wr, DECODE_KERNEL)
+        ff, _ = _mean_of(F, FUSED_DECODE_KERNEL)
+        fw, _ = _mean_of(Wr, FUSED_DECODE_KERNEL)
+        mf, _ = _mean_of(F, MULTI_DECODE_KERNEL)
+        mw, _ = _mean_of(Wr, MULTI_DECODE_KERNEL)
+        rec = {"kernel": DECODE_KERNEL,
+               "workload": "decode B=4096, Hk=Hv=32, K=V=128, bf16 q/k/v, fp32 pool 4160 slots",
+               "fetch_size_kib": f, "write_size_kib": w, **common,
+               "traffic_bytes_per_launch": both(f, w),
+               "algorithmic_bytes_per_launch": decode_work(4096, 32, 32, 128, 128),
+               "fused_gate_kernel": FUSED_DECODE_KERNEL,
+               "fused_gate_fetch_size_kib_mean": ff, "fused_gate_write_size_kib_mean": fw,
+               "fused_gate_traffic_bytes_per_launch": both(ff, fw),
+               "fused_gate_algorithmic_bytes_per_launch": decode_work(4096, 32, 32, 128, 128, gate_bytes=2),
+               "multi_decode_kernel": MULTI_DECODE_KERNEL,
+               "multi_decode_workload": "verify: 1024 requests x 4 tokens, Hv=32, K=V=128, fused gate, fp32 pool "
+                                        "read-only, fp32 cache pitch 8",
+               "multi_decode_fetch_size_kib_mean": mf, "multi_decode_write_size_kib_mean": mw,
+               "multi_decode_traffic_bytes_per_launch": both(mf, mw),
+               "multi_decode_algorithmic_bytes_per_launch": multi_decode_work([4] * 1024, 32, 32, 128, 128, 8,
+                                                                              False),
+               "kernel_source_sha256_16": _sha(DECODE_SRC), "commands": cmds}
+        path = path or TRAFFIC_FILE
+    else:
+        import kda_workloads as W
+        cu = W.kimi_prefill_16seq().cu_seqlens.tolist()
+        kern = {}
+        for nm, key in PREFILL_KERNELS:
+            f, calls = _mean_of(F, key)
+            w, _ = _mean_of(Wr, key)
+            kern[nm] = {"kernel": "kda::" + key, "calls": calls, "fetch_size_kib_mean": f, "write_size_kib_mean": w,
+                        "read_bytes": f * fs * 1024, "written_bytes": w * ws * 1024}
+        tot = lambda names: sum(kern[n]["read_bytes"] + kern[n]["written_bytes"] for n in names)
+        rec = {"workload": "prefill: 16 sequences, lengths U{512..4096} (T=%d), Hk=Hv=32, K=V=128, bf16 q/k/v, "
+                           "fp32 g and beta, fp32 pool of 32 slots" % cu[-1],
+               **common, "kernels": kern,
+               "traffic_bytes_per_call": tot(["meta", "intra", "state"]),
+               "algorithmic_bytes_per_call": prefill_work(cu, 32, 32, 128, 128)[1],
+               "fused_gate_traffic_bytes_per_call": tot(["meta", "intra_fused_gate", "state"]),
+               "fused_gate_algorithmic_bytes_per_call": prefill_work(cu, 32, 32, 128, 128, gate_bytes=2)[1],
+               "kernel_source_sha256_16": _sha(PREFILL_SRC), "commands": cmds}
+        path = path or PREFILL_TRAFFIC_FILE
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("wrote %s" % path)
+    return rec
+
+
 def cpu_model():
     """The host CPU's model name, from /proc/cpuinfo."""
     try:
@@ -175,7 +281,17 @@ def main():
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="run one plain device copy of this size first (a known-size "
                          "reference for FETCH_SIZE / WRITE_SIZE counter runs)")
+    ap.add_argument("--traffic-record", choices=["prefill", "decode"],
+                    help="no timing: write that part's traffic record under profiles/ from two "
+                         "rocprofv3 --pmc runs (--fetch-dir, --write-dir) and exit")
+    ap.add_argument("--fetch-dir", help="rocprofv3 -d directory of the FETCH_SIZE run")
+    ap.add_argument("--write-dir", help="rocprofv3 -d directory of the WRITE_SIZE run")
     args = ap.parse_args()
+    if args.traffic_record:
+        if not (args.fetch_dir and args.write_dir):
+            ap.error("--traffic-record needs --fetch-dir and --write-dir")
+        traffic_record(args.traffic_record, args.fetch_dir, args.write_dir)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: (sequence, head) and (request, head) units are "
               "independent, so more GPUs would each run this same path on their own heads or "
