@@ -15,7 +15,7 @@ the kernels) and reported under "fused_gate", and a multi-token verify decode
 (1024 requests x 4 tokens with a per-step state cache) is timed and reported
 under "spec_decode".  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
 
 The traffic records under profiles/ (HBM bytes counted by rocprofv3) are
 written by ``--traffic-record``, from counter runs of this script.
@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -104,43 +105,50 @@ def cpu_baseline(pre, dec, reps=5, nreq=1024):
     """The fp64 oracle on the host cores, on a bounded sample of the same
     workload: the full prefill batch (all 16 sequences, all heads; median of
     ``reps`` runs) and the first ``nreq`` of the 4096 decode requests (median of
-    3 runs)."""
-    import statistics
+    3 runs).  The inputs are converted to the oracle's array types before
+    the clock starts, so each time covers the oracle's computation only."""
     from oracle import oracle as O
     O.build(force=False)
     threads = O.max_threads()
+    f32 = lambda x: x.float().contiguous().numpy()
+    f64 = lambda x: x.double().contiguous().numpy()
     slots = O.map_slot(pre.indices.numpy(), pre.pool.shape[0])
     h0 = pre.pool[slots]
+    P = (f32(pre.q), f32(pre.k), f32(pre.v), f64(pre.g), f64(pre.beta), pre.cu_seqlens.numpy())
+    h0n = f32(h0)
     tps = []
     for _ in range(reps):
         t = time.perf_counter()
-        O.prefill(pre.q, pre.k, pre.v, pre.g, pre.beta, pre.cu_seqlens, h0=h0)
+        O.prefill(*P, h0=h0n)
         tps.append(time.perf_counter() - t)
     tp = statistics.median(tps)
     T = int(pre.cu_seqlens[-1])
     dslots = O.map_slot(dec.indices.numpy()[:nreq], dec.pool.shape[0])
-    pool = dec.pool[dslots]
+    D = (f32(dec.q[:nreq]), f32(dec.k[:nreq]), f32(dec.v[:nreq]), f64(dec.g[:nreq]), f64(dec.beta[:nreq]))
+    pool = f32(dec.pool[dslots])
     tds = []
     for _ in range(3):
         t = time.perf_counter()
-        O.decode(dec.q[:nreq], dec.k[:nreq], dec.v[:nreq], dec.g[:nreq], dec.beta[:nreq], pool)
+        O.decode(*D, pool)
         tds.append(time.perf_counter() - t)
     td = statistics.median(tds)
     hv = dec.v.shape[1]
     # one thread, on the first `h1` heads of every sequence (heads are
     # independent units of equal cost), scaled to all heads
     h1 = 4
-    sel = lambda x: x[:, :h1].contiguous()
+    sel = lambda x: x[:, :h1]
+    P1 = (f32(sel(pre.q)), f32(sel(pre.k)), f32(sel(pre.v)), f64(sel(pre.g)), f64(sel(pre.beta)),
+          pre.cu_seqlens.numpy())
+    h01 = f32(sel(h0))
     t = time.perf_counter()
-    O.prefill(sel(pre.q), sel(pre.k), sel(pre.v), sel(pre.g), sel(pre.beta), pre.cu_seqlens, h0=sel(h0),
-              nthreads=1)
+    O.prefill(*P1, h0=h01, nthreads=1)
     t1 = (time.perf_counter() - t) * hv / h1
     return {
         "value": T / tp, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "sample": "fp64 C oracle (OpenMP over sequence-head units): full prefill batch "
                   "(%d tokens x 32 heads), median of %d runs = %.2f s; decode: first %d of 4096 "
                   "requests, median of 3 runs = %.3f s; one thread: the first %d heads of the "
-                  "prefill batch, scaled to 32 heads" % (T, reps, tp, nreq, td, h1),
+                  "prefill batch, scaled to 32 heads; inputs converted before timing" % (T, reps, tp, nreq, td, h1),
         "decode_states_per_s": nreq * hv / td,
         "one_thread_value": T / t1,
         "cpu_model": cpu_model(),
@@ -267,7 +275,7 @@ def cpu_model():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--spec-steps", type=int, default=10,
@@ -360,8 +368,9 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    pre_t = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_t = [e[1].elapsed_time(e[2]) for e in evs]
+    pre_ms, dec_ms = sum(pre_t) / args.steps, sum(dec_t) / args.steps
 
     # fused-gate variant, timed after the step loop (not part of the step)
     fsteps = args.fused_gate_steps
@@ -420,14 +429,16 @@ def main():
     B = dec.q.shape[0] if do_dec else 0
     db = decode_work(B, hk, hv, dk, dv)
 
-    prefill = {"ms": pre_ms, "tokens_per_s": T / (pre_ms * 1e-3) if do_pre else None,
+    prefill = {"ms": pre_ms, "ms_median": statistics.median(pre_t),
+               "tokens_per_s": T / (pre_ms * 1e-3) if do_pre else None,
                "tokens": T, "alg_tflops": pf / (pre_ms * 1e-3) / 1e12 if do_pre else None,
                "alg_gbs": pb / (pre_ms * 1e-3) / 1e9 if do_pre else None}
     if do_pre:
         prefill["mfma_frac_alg"] = prefill["alg_tflops"] / MFMA_F16_PEAK_TFLOPS
         prefill["hbm_frac_alg"] = prefill["alg_gbs"] / HBM_PEAK_GBS
         prefill["roofline_frac"] = max(pf / (MFMA_F16_PEAK_TFLOPS * 1e12), pb / (HBM_PEAK_GBS * 1e9)) / (pre_ms * 1e-3)
-    decode = {"ms": dec_ms, "states_per_s": B * hv / (dec_ms * 1e-3) if do_dec else None,
+    decode = {"ms": dec_ms, "ms_median": statistics.median(dec_t),
+              "states_per_s": B * hv / (dec_ms * 1e-3) if do_dec else None,
               "requests_per_s": B / (dec_ms * 1e-3) if do_dec else None,
               "alg_gbs": db / (dec_ms * 1e-3) / 1e9 if do_dec else None}
     if do_dec:
