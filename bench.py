@@ -272,6 +272,15 @@ def cpu_model():
     return "unknown"
 
 
+def workload_name(part, long_prompt, T):
+    pre = ("KDA chunked prefill: 1 sequence of %d tokens, Hk=Hv=32, K=V=128, bf16 q/k/v, realistic "
+           "per-channel gates, fp32 pool 2 slots" % T if long_prompt else
+           "KDA chunked prefill: 16 seqs, lengths U{512..4096} (T=%d), Hk=Hv=32, K=V=128, bf16 q/k/v, "
+           "realistic per-channel gates, fp32 pool 32 slots" % T)
+    dec = "recurrent decode: B=4096, Hk=Hv=32, K=V=128, fp32 pool 4160 slots"
+    return {"both": pre + "; + " + dec, "prefill": pre, "decode": dec}[part]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +295,9 @@ def main():
                          "entry points (0: skip)")
     ap.add_argument("--part", choices=["both", "prefill", "decode"], default="both",
                     help="time one part only (for profiling runs)")
+    ap.add_argument("--prefill-workload", choices=["16seq", "long"], default="16seq",
+                    help="16seq: 16 sequences of 512-4096 tokens (the step's prefill); long: one "
+                         "sequence of 32,768 tokens, 32 heads (a measurement of its own)")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="run one plain device copy of this size first (a known-size "
                          "reference for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -295,6 +307,9 @@ def main():
     ap.add_argument("--fetch-dir", help="rocprofv3 -d directory of the FETCH_SIZE run")
     ap.add_argument("--write-dir", help="rocprofv3 -d directory of the WRITE_SIZE run")
     args = ap.parse_args()
+    long_prompt = args.prefill_workload == "long"
+    if long_prompt and args.part != "prefill":
+        ap.error("--prefill-workload long is timed on its own: add --part prefill")
     if args.traffic_record:
         if not (args.fetch_dir and args.write_dir):
             ap.error("--traffic-record needs --fetch-dir and --write-dir")
@@ -316,7 +331,7 @@ def main():
 
     do_pre = args.part in ("both", "prefill")
     do_dec = args.part in ("both", "decode")
-    pre = W.kimi_prefill_16seq() if do_pre else None
+    pre = (W.long_prompt_32k() if long_prompt else W.kimi_prefill_16seq()) if do_pre else None
     dec = W.decode_b4096() if do_dec else None
     names = ("q", "k", "v", "g", "beta", "gx", "A_log", "dt_bias", "bx", "pool", "indices")
     P = {n: getattr(pre, n).to(dev) for n in names + ("cu_seqlens",)} if do_pre else {}
@@ -461,7 +476,8 @@ def main():
     # dominant kernel: the decode kernel (one launch per step, timed by the
     # events that bracket it on the stream it runs on)
     if do_pre:
-        ptr = measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRC)
+        # (the record covers the 16-sequence workload only)
+        ptr = None if long_prompt else measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRC)
         # counted HBM bytes of one prefill call (meta, intra and state kernels)
         # and their ratio to the algorithmic bytes
         prefill["traffic"] = ptr.get("traffic_bytes_per_call") if ptr else None
@@ -487,9 +503,7 @@ def main():
         "ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "KDA chunked prefill: 16 seqs, lengths U{512..4096} (T=%d), Hk=Hv=32, "
-                               "K=V=128, bf16 q/k/v, realistic per-channel gates, fp32 pool 32 slots; "
-                               "+ recurrent decode: B=4096, Hk=Hv=32, K=V=128, fp32 pool 4160 slots" % T,
+        "config": {"workload": workload_name(args.part, long_prompt, T),
                    "global_batch": len(cu) - 1, "seq_len": T, "parallelism": "single-gpu"},
         "prefill": prefill, "decode": decode, "roofline": roof, "finite": finite,
         "fused_gate": fused, "spec_decode": spec,

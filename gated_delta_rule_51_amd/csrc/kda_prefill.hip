@@ -108,7 +108,9 @@ struct Work {
 __global__ __launch_bounds__(1024) void meta_kernel(const int32_t *cu, int n, Work w) {
     __shared__ int32_t part[1024];
     __shared__ int32_t carry;
+    __shared__ int32_t off[kOrderMax + 1];   // chunk offsets, when n <= kOrderMax
     const int tid = threadIdx.x;
+    const bool staged = n <= kOrderMax;
     if (tid == 0) carry = 0;
     __syncthreads();
     for (int base = 0; base < n; base += 1024) {
@@ -120,8 +122,8 @@ __global__ __launch_bounds__(1024) void meta_kernel(const int32_t *cu, int n, Wo
         }
         part[tid] = cnt;
         __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {   // inclusive scan
-            const int x = tid >= off ? part[tid - off] : 0;
+        for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
+            const int x = tid >= o ? part[tid - o] : 0;
             __syncthreads();
             part[tid] += x;
             __syncthreads();
@@ -129,7 +131,9 @@ __global__ __launch_bounds__(1024) void meta_kernel(const int32_t *cu, int n, Wo
         const int excl = carry + part[tid] - cnt;
         if (s < n) {
             w.chunk_off[s] = excl;
-            for (int j = 0; j < cnt && excl + j < w.slots; ++j) w.chunk_map[excl + j] = make_int2(s, j);
+            if (staged) off[s] = excl;
+            else   // (each thread fills its own sequences' entries)
+                for (int j = 0; j < cnt && excl + j < w.slots; ++j) w.chunk_map[excl + j] = make_int2(s, j);
         }
         __syncthreads();
         if (tid == 1023) carry += part[1023];
@@ -137,7 +141,29 @@ __global__ __launch_bounds__(1024) void meta_kernel(const int32_t *cu, int n, Wo
     }
     const int total = carry;
     if (tid == 0) w.chunk_off[n] = total;
-    for (int s = total + tid; s < w.slots; s += 1024) w.chunk_map[s] = make_int2(-1, -1);
+    if (staged) {
+        // One chunk slot per thread: its sequence is the last one whose first
+        // chunk slot is at or before it (binary search over the staged
+        // offsets; empty sequences share the next one's offset and are
+        // passed over), so one long sequence does not leave one thread to
+        // write all of its entries.
+        __syncthreads();
+        for (int c = tid; c < w.slots; c += 1024) {
+            int2 e = make_int2(-1, -1);
+            if (c < total) {
+                int lo = 0, hi = n - 1;   // off[lo] <= c holds throughout
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (off[mid] <= c) lo = mid;
+                    else hi = mid - 1;
+                }
+                e = make_int2(lo, c - off[lo]);
+            }
+            w.chunk_map[c] = e;
+        }
+    } else {
+        for (int c = total + tid; c < w.slots; c += 1024) w.chunk_map[c] = make_int2(-1, -1);
+    }
 
     // Longest sequences first, so the state kernel's long sequential chains
     // start in the first wave of workgroups (ties keep index order).  Counting

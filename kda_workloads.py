@@ -183,6 +183,13 @@ def kimi_prefill_16seq(seed=4):
                         pool_slots=32)
 
 
+def long_prompt_32k(seed=12):
+    """One long prompt: a single sequence of 32,768 tokens, Hk=Hv=32,
+    K=V=128, bf16 io, realistic gates, fp32 pool of 2 slots (32 chains, each
+    512 chunks long)."""
+    return make_prefill(seed, [32768], 32, 32, 128, 128, gate="realistic", pool_slots=2)
+
+
 def gdn_pool_page(seed=11, state_dtype="f32", pad_one=False):
     """The GDN pool-mode test recipe of the sglang PR 30169 digest (key-code
     test): 5 sequences of randint(1, 130) tokens, Hk = 4, Hv = 8, K = V = 128,
