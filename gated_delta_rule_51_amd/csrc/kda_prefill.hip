@@ -166,20 +166,97 @@ __global__ __launch_bounds__(1024) void meta_kernel(const int32_t *cu, int n, Wo
     }
 
     // Longest sequences first, so the state kernel's long sequential chains
-    // start in the first wave of workgroups (ties keep index order).  Counting
-    // ranks is O(N^2); beyond kOrderMax sequences the natural order is kept.
-    if (n <= kOrderMax) {
-        __shared__ int32_t len[kOrderMax];   // lengths staged once: the rank loop reads LDS
-        for (int s = tid; s < n; s += 1024) len[s] = cu[s + 1] - cu[s];
-        __syncthreads();
-        for (int s = tid; s < n; s += 1024) {
-            const int ls = len[s];
-            int rank = 0;
-            for (int m = 0; m < n; ++m) {
-                const int lm = len[m];
-                rank += (lm > ls) || (lm == ls && m < s);
+    // start in the first wave of workgroups; equal lengths (and lengths past
+    // kLenCap tokens) keep index order.  The order sorts the unique keys
+    // ((kLenCap - length) << 12) | index.  Up to kRankMax sequences a thread
+    // per sequence counts the keys below its own.  Beyond that, a bitonic
+    // sort of the keys padded to a power of two P: thread t holds elements
+    // 4t .. 4t+3, so partners up to 2 apart are in its own registers, up to
+    // 128 apart in another lane of its wave (lane shuffles), and only those
+    // 256 or more apart go through LDS, with a barrier per pass.  Beyond
+    // kOrderMax sequences the natural order is kept.
+    static_assert(kOrderMax == 4 * 1024, "four keys per thread; 12-bit index");
+    constexpr uint32_t kLenCap = (1u << 20) - 2;   // the largest key stays below the padding key
+    constexpr int kRankMax = 512;
+    if (staged) {
+        __shared__ __align__(16) uint32_t key[kOrderMax];
+        auto make_key = [&](int i) -> uint32_t {
+            const uint32_t len = (uint32_t)min(max(cu[i + 1] - cu[i], 0), (int)kLenCap);
+            return ((kLenCap - len) << 12) | (uint32_t)i;
+        };
+        if (n <= kRankMax) {
+            for (int i = tid; i < ((n + 3) & ~3); i += 1024) key[i] = i < n ? make_key(i) : ~0u;
+            __syncthreads();
+            if (tid < n) {
+                const uint32_t ks = key[tid];
+                int rank = 0;
+                for (int m = 0; m < n; m += 4) {
+                    const u32x4 km = *reinterpret_cast<const u32x4 *>(key + m);
+                    rank += (km[0] < ks) + (km[1] < ks) + (km[2] < ks) + (km[3] < ks);
+                }
+                w.seq_order[rank] = tid;
             }
-            w.seq_order[rank] = s;
+        } else {
+            int P = 1;
+            while (P < n) P <<= 1;
+            const int lane = tid & 63;
+            uint32_t x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = 4 * tid + e < n ? make_key(4 * tid + e) : ~0u;
+            for (int k = 2; k <= P; k <<= 1) {
+                int j = k >> 1;
+                if (j >= 256) {   // partners in other waves
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) key[4 * tid + e] = x[e];
+                    __syncthreads();
+                    for (; j >= 256; j >>= 1) {
+                        for (int i = tid; i < P; i += 1024) {
+                            const int ixj = i ^ j;
+                            if (ixj > i) {
+                                const uint32_t a = key[i], b = key[ixj];
+                                if ((a > b) == ((i & k) == 0)) {
+                                    key[i] = b;
+                                    key[ixj] = a;
+                                }
+                            }
+                        }
+                        __syncthreads();
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = key[4 * tid + e];
+                    __syncthreads();
+                }
+                for (; j >= 4; j >>= 1) {   // partners in lane tid ^ (j / 4) of this wave
+                    const int m = j >> 2;
+                    const bool lower = (lane & m) == 0;
+                    uint32_t y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = __shfl_xor(x[e], m, 64);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool keep_min = lower == (((4 * tid + e) & k) == 0);
+                        x[e] = keep_min ? min(x[e], y[e]) : max(x[e], y[e]);
+                    }
+                }
+                // partners in this thread (j = 2, then 1)
+#pragma unroll
+                for (int jj = 2; jj >= 1; jj >>= 1) {
+                    if (jj <= j) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if ((e & jj) == 0) {
+                                const uint32_t a = x[e], b = x[e | jj];
+                                const bool asc = ((4 * tid + e) & k) == 0;
+                                x[e] = asc ? min(a, b) : max(a, b);
+                                x[e | jj] = asc ? max(a, b) : min(a, b);
+                            }
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * tid + e < n) w.seq_order[4 * tid + e] = (int32_t)(x[e] & 0xfffu);
         }
     } else {
         for (int s = tid; s < n; s += 1024) w.seq_order[s] = s;

@@ -69,7 +69,7 @@ def test_wide_gqa(K, oracle):
     run_and_check(K, oracle, inp, "gqa 1:8")
 
 
-@pytest.mark.parametrize("n", [300, 4200])
+@pytest.mark.parametrize("n", [300, 4096, 4200])
 def test_many_short_sequences(K, oracle, n):
     g = torch.Generator().manual_seed(75 + n)
     lens = torch.randint(0, 5, (n,), generator=g).tolist()
