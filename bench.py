@@ -123,6 +123,7 @@ def cpu_baseline(pre, dec, reps=5, nreq=1024):
         tps.append(time.perf_counter() - t)
     tp = statistics.median(tps)
     T = int(pre.cu_seqlens[-1])
+    nreq = min(nreq, dec.q.shape[0])
     dslots = O.map_slot(dec.indices.numpy()[:nreq], dec.pool.shape[0])
     D = (f32(dec.q[:nreq]), f32(dec.k[:nreq]), f32(dec.v[:nreq]), f64(dec.g[:nreq]), f64(dec.beta[:nreq]))
     pool = f32(dec.pool[dslots])
@@ -146,9 +147,10 @@ def cpu_baseline(pre, dec, reps=5, nreq=1024):
     return {
         "value": T / tp, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "sample": "fp64 C oracle (OpenMP over sequence-head units): full prefill batch "
-                  "(%d tokens x 32 heads), median of %d runs = %.2f s; decode: first %d of 4096 "
+                  "(%d tokens x 32 heads), median of %d runs = %.2f s; decode: first %d of %d "
                   "requests, median of 3 runs = %.3f s; one thread: the first %d heads of the "
-                  "prefill batch, scaled to 32 heads; inputs converted before timing" % (T, reps, tp, nreq, td, h1),
+                  "prefill batch, scaled to 32 heads; inputs converted before timing"
+                  % (T, reps, tp, nreq, dec.q.shape[0], td, h1),
         "decode_states_per_s": nreq * hv / td,
         "one_thread_value": T / t1,
         "cpu_model": cpu_model(),
@@ -272,12 +274,12 @@ def cpu_model():
     return "unknown"
 
 
-def workload_name(part, long_prompt, T):
+def workload_name(part, long_prompt, T, B=4096):
     pre = ("KDA chunked prefill: 1 sequence of %d tokens, Hk=Hv=32, K=V=128, bf16 q/k/v, realistic "
            "per-channel gates, fp32 pool 2 slots" % T if long_prompt else
            "KDA chunked prefill: 16 seqs, lengths U{512..4096} (T=%d), Hk=Hv=32, K=V=128, bf16 q/k/v, "
            "realistic per-channel gates, fp32 pool 32 slots" % T)
-    dec = "recurrent decode: B=4096, Hk=Hv=32, K=V=128, fp32 pool 4160 slots"
+    dec = "recurrent decode: B=%d, Hk=Hv=32, K=V=128, fp32 pool %d slots" % (B, B + 64)
     return {"both": pre + "; + " + dec, "prefill": pre, "decode": dec}[part]
 
 
@@ -293,6 +295,10 @@ def main():
     ap.add_argument("--fused-gate-steps", type=int, default=10,
                     help="after the timed steps, time this many passes through the fused-gate "
                          "entry points (0: skip)")
+    ap.add_argument("--decode-batch", type=int, default=4096,
+                    help="requests of the one-token decode (pool of batch + 64 slots)")
+    ap.add_argument("--spec-batch", type=int, default=1024,
+                    help="requests of the verify decode (4 tokens each; pool of batch + 64 slots)")
     ap.add_argument("--part", choices=["both", "prefill", "decode"], default="both",
                     help="time one part only (for profiling runs)")
     ap.add_argument("--prefill-workload", choices=["16seq", "long"], default="16seq",
@@ -332,7 +338,7 @@ def main():
     do_pre = args.part in ("both", "prefill")
     do_dec = args.part in ("both", "decode")
     pre = (W.long_prompt_32k() if long_prompt else W.kimi_prefill_16seq()) if do_pre else None
-    dec = W.decode_b4096() if do_dec else None
+    dec = W.decode_b4096(batch=args.decode_batch, num_slots=args.decode_batch + 64) if do_dec else None
     names = ("q", "k", "v", "g", "beta", "gx", "A_log", "dt_bias", "bx", "pool", "indices")
     P = {n: getattr(pre, n).to(dev) for n in names + ("cu_seqlens",)} if do_pre else {}
     D = {n: getattr(dec, n).to(dev) for n in names} if do_dec else {}
@@ -402,7 +408,7 @@ def main():
     # multi-token verify decode (speculative decoding), timed on its own
     spec = None
     if args.spec_steps > 0 and do_dec:
-        m = W.spec_decode_b1024()
+        m = W.spec_decode_b1024(batch=args.spec_batch, num_slots=args.spec_batch + 64)
         t = m.tok
         S = {n: getattr(t, n).to(dev) for n in ("q", "k", "v", "gx", "A_log", "dt_bias", "bx", "cu_seqlens")}
         spool, sidx = m.pool.to(dev), m.indices.to(dev)
@@ -429,8 +435,9 @@ def main():
         spec_ms = sum(e[0].elapsed_time(e[1]) for e in sev) / args.spec_steps
         lens = (t.cu_seqlens[1:] - t.cu_seqlens[:-1]).tolist()
         sb = multi_decode_work(lens, t.q.shape[1], hv_, dk_, dv_, m.cache_pitch, False)
-        spec = {"workload": "multi-token verify decode: 1024 requests x 4 tokens, Hk=Hv=32, K=V=128, bf16 io, "
-                            "fused gate, fp32 pool 1088 slots read-only, fp32 step cache pitch 8",
+        spec = {"workload": "multi-token verify decode: %d requests x 4 tokens, Hk=Hv=32, K=V=128, bf16 io, "
+                            "fused gate, fp32 pool %d slots read-only, fp32 step cache pitch 8"
+                            % (args.spec_batch, args.spec_batch + 64),
                 "steps": args.spec_steps, "ms": spec_ms,
                 "tokens_per_s": sum(lens) / (spec_ms * 1e-3),
                 "alg_bytes_per_launch": sb, "alg_gbs": sb / (spec_ms * 1e-3) / 1e9,
@@ -483,7 +490,8 @@ def main():
         prefill["traffic"] = ptr.get("traffic_bytes_per_call") if ptr else None
         prefill["traffic_over_alg"] = prefill["traffic"] / pb if prefill["traffic"] else None
     if do_dec:
-        dtr = measured_traffic()
+        # (the record covers the 4096-request workload only)
+        dtr = measured_traffic() if B == 4096 else None
         roof = {"kernel": DECODE_KERNEL, "bound": "hbm",
                 "achieved": decode["alg_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": decode["alg_gbs"] / HBM_PEAK_GBS,
@@ -503,7 +511,7 @@ def main():
         "ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16", "data": "synthetic",
-        "config": {"workload": workload_name(args.part, long_prompt, T),
+        "config": {"workload": workload_name(args.part, long_prompt, T, B),
                    "global_batch": len(cu) - 1, "seq_len": T, "parallelism": "single-gpu"},
         "prefill": prefill, "decode": decode, "roofline": roof, "finite": finite,
         "fused_gate": fused, "spec_decode": spec,

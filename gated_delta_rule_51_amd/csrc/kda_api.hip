@@ -185,7 +185,7 @@ kda_status decode_impl(const kda_decode_desc *d, const void *q, const void *k, c
         hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_z, hipDeviceAttributeMaxGridDimZ, dev) != hipSuccess)
         return KDA_ERR_HIP;
-    const long xdim = (long)d->hv * (d->dv / kda::decode_tile(d->dv));
+    const long xdim = (long)d->hv * (d->dv / kda::decode_tile(d->dv, d->batch, d->hv, false));
     if (xdim > max_x || kda::decode_grid_y(d->batch) > max_y || kda::decode_grid_z(d->batch) > max_z)
         return KDA_ERR_UNSUPPORTED;
 
@@ -259,7 +259,7 @@ kda_status multi_decode_impl(const kda_multi_decode_desc *d, const void *q, cons
         hipDeviceGetAttribute(&max_y, hipDeviceAttributeMaxGridDimY, dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_z, hipDeviceAttributeMaxGridDimZ, dev) != hipSuccess)
         return KDA_ERR_HIP;
-    const long xdim = (long)d->hv * (d->dv / kda::decode_tile(d->dv));
+    const long xdim = (long)d->hv * (d->dv / kda::decode_tile(d->dv, d->batch, d->hv, true));
     if (xdim > max_x || kda::decode_grid_y(d->batch) > max_y || kda::decode_grid_z(d->batch) > max_z)
         return KDA_ERR_UNSUPPORTED;
 

@@ -358,7 +358,7 @@ static hipError_t launch_v(const DecodeArgs &a, int bv, bool m, hipStream_t s) {
 }
 
 static hipError_t launch_any(const DecodeArgs &a, bool multi, hipStream_t stream) {
-    const int bv = decode_tile(a.dv);
+    const int bv = decode_tile(a.dv, a.batch, a.hv, multi);
     switch (a.dk) {
     case 32: return launch_v<32>(a, bv, multi, stream);
     case 64: return launch_v<64>(a, bv, multi, stream);
@@ -373,9 +373,20 @@ int decode_grid_y(int batch) {
     return batch <= 0 ? 1 : (batch + z - 1) / z;
 }
 
-// Whole head per workgroup (up to 128 value rows): measured fastest on MI355X
-// (K = V = 128, B = 4096, Hv = 32: 3.0 ms vs 3.3 ms with 64-row tiles).
-int decode_tile(int dv) { return dv < 128 ? dv : 128; }
+// Value rows per workgroup.  A whole head (up to 128 rows) once the batch
+// fills the chip; 32-row tiles for small batches, where four times as many
+// shorter workgroups cut the latency.  Kernel times on MI355X (K = V = 128,
+// Hv = 32), whole head against 32-row tiles: one-token decode B = 1 9.2 and
+// 4.4 us, B = 16 16.9 and 12.5 us, B = 256 198 and 188 us, B = 512 374 and
+// 385 us, B = 4096 2.87 and 3.21 ms; verify with 4 tokens per request B = 1
+// 29 and 10 us, B = 16 41 and 32 us, B = 64 124 and 130 us.  The results
+// are the same either way (a row's arithmetic does not depend on its tile).
+int decode_tile(int dv, long batch, int hv, bool multi) {
+    const long rows = batch * hv * (long)dv;   // state rows of the call
+    const long small = (multi ? 32L : 256L) * 32 * 128;
+    if (dv > 32 && rows <= small) return 32;
+    return dv < 128 ? dv : 128;
+}
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) { return launch_any(a, false, stream); }
 

@@ -31,7 +31,7 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeArgs &a, hipStream_t stream);
-int decode_tile(int dv);
+int decode_tile(int dv, long batch, int hv, bool multi);
 int decode_grid_y(int batch);   // requests per z slab of the decode grid
 int decode_grid_z(int batch);   // z slabs
 
