@@ -108,6 +108,12 @@ __device__ __forceinline__ void store_rows(ST *st, const unsigned (&ro)[RowTile<
     }
 }
 
+// Cache policy of the state stores that stream out of the verify decode: the
+// nontemporal and device-scope bits (nt, sc1).  Its cached steps measured on
+// MI355X (1024 requests x 4 tokens): nt alone 1.885 ms, nt with sc1
+// 1.842 ms, sc0 with sc1 and no nt 2.10 ms.
+constexpr int kStreamStore = 2 | 16;
+
 // Store this thread's part of the rows through a buffer resource covering the
 // row block: the lane's offset is one register and each pass adds a scalar
 // offset, so the stores need no address arithmetic between them and go out
@@ -127,7 +133,7 @@ __device__ __forceinline__ void store_rows_buf(const __amdgpu_buffer_rsrc_t rsrc
 #pragma unroll
                 for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(s[p][2 * i], s[p][2 * i + 1]);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(w, rsrc, voff, p * R::RPP * DK * (int)sizeof(ST), 2);
+            __builtin_amdgcn_raw_buffer_store_b128(w, rsrc, voff, p * R::RPP * DK * (int)sizeof(ST), kStreamStore);
         }
     }
 }
