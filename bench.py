@@ -274,7 +274,10 @@ def cpu_model():
     return "unknown"
 
 
-def workload_name(part, long_prompt, T, B=4096):
+def workload_name(part, long_prompt, T, B=4096, lengths=None):
+    if lengths:
+        return ("KDA chunked prefill: %d sequences of lengths %s (T=%d), Hk=Hv=32, K=V=128, bf16 q/k/v, "
+                "realistic per-channel gates, fp32 pool %d slots" % (len(lengths), lengths, T, len(lengths) + 1))
     pre = ("KDA chunked prefill: 1 sequence of %d tokens, Hk=Hv=32, K=V=128, bf16 q/k/v, realistic "
            "per-channel gates, fp32 pool 2 slots" % T if long_prompt else
            "KDA chunked prefill: 16 seqs, lengths U{512..4096} (T=%d), Hk=Hv=32, K=V=128, bf16 q/k/v, "
@@ -301,6 +304,9 @@ def main():
                     help="requests of the verify decode (4 tokens each; pool of batch + 64 slots)")
     ap.add_argument("--part", choices=["both", "prefill", "decode"], default="both",
                     help="time one part only (for profiling runs)")
+    ap.add_argument("--prefill-lengths", default=None,
+                    help="comma-separated sequence lengths for a prefill of their own (32 heads, "
+                         "K=V=128, bf16, realistic gates, fp32 pool), with --part prefill")
     ap.add_argument("--prefill-workload", choices=["16seq", "long"], default="16seq",
                     help="16seq: 16 sequences of 512-4096 tokens (the step's prefill); long: one "
                          "sequence of 32,768 tokens, 32 heads (a measurement of its own)")
@@ -314,8 +320,9 @@ def main():
     ap.add_argument("--write-dir", help="rocprofv3 -d directory of the WRITE_SIZE run")
     args = ap.parse_args()
     long_prompt = args.prefill_workload == "long"
-    if long_prompt and args.part != "prefill":
-        ap.error("--prefill-workload long is timed on its own: add --part prefill")
+    if (long_prompt or args.prefill_lengths) and args.part != "prefill":
+        ap.error("--prefill-workload long and --prefill-lengths are timed on their own: add --part prefill")
+    lengths = [int(x) for x in args.prefill_lengths.split(",")] if args.prefill_lengths else None
     if args.traffic_record:
         if not (args.fetch_dir and args.write_dir):
             ap.error("--traffic-record needs --fetch-dir and --write-dir")
@@ -337,7 +344,12 @@ def main():
 
     do_pre = args.part in ("both", "prefill")
     do_dec = args.part in ("both", "decode")
-    pre = (W.long_prompt_32k() if long_prompt else W.kimi_prefill_16seq()) if do_pre else None
+    if not do_pre:
+        pre = None
+    elif lengths:
+        pre = W.make_prefill(12, lengths, 32, 32, 128, 128, gate="realistic", pool_slots=len(lengths) + 1)
+    else:
+        pre = W.long_prompt_32k() if long_prompt else W.kimi_prefill_16seq()
     dec = W.decode_b4096(batch=args.decode_batch, num_slots=args.decode_batch + 64) if do_dec else None
     names = ("q", "k", "v", "g", "beta", "gx", "A_log", "dt_bias", "bx", "pool", "indices")
     P = {n: getattr(pre, n).to(dev) for n in names + ("cu_seqlens",)} if do_pre else {}
@@ -484,7 +496,7 @@ def main():
     # events that bracket it on the stream it runs on)
     if do_pre:
         # (the record covers the 16-sequence workload only)
-        ptr = None if long_prompt else measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRC)
+        ptr = None if (long_prompt or lengths) else measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRC)
         # counted HBM bytes of one prefill call (meta, intra and state kernels)
         # and their ratio to the algorithmic bytes
         prefill["traffic"] = ptr.get("traffic_bytes_per_call") if ptr else None
@@ -511,7 +523,7 @@ def main():
         "ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16", "data": "synthetic",
-        "config": {"workload": workload_name(args.part, long_prompt, T, B),
+        "config": {"workload": workload_name(args.part, long_prompt, T, B, lengths),
                    "global_batch": len(cu) - 1, "seq_len": T, "parallelism": "single-gpu"},
         "prefill": prefill, "decode": decode, "roofline": roof, "finite": finite,
         "fused_gate": fused, "spec_decode": spec,
