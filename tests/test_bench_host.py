@@ -1,6 +1,6 @@
 """Host-side logic of bench.py (CPU only): the algorithmic byte counts the
-roofline uses, the traffic record written from rocprofv3 counter files, and
-the one-GPU guard."""
+roofline uses, the traffic record written from rocprofv3 counter files, the
+one-GPU guard, and the workload options' checks and names."""
 import csv
 import json
 import os
@@ -93,3 +93,24 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("args", [["--prefill-workload", "long"], ["--prefill-lengths", "64,128"],
+                                  ["--prefill-lengths", "64", "--part", "decode"]])
+def test_own_prefill_workloads_need_part_prefill(args):
+    """The long-prompt and given-lengths prefills are timed on their own; the
+    step (prefill + decode) keeps its fixed workloads."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "--part prefill" in r.stderr
+
+
+def test_workload_names():
+    assert bench.workload_name("decode", False, 0, 256).startswith("recurrent decode: B=256,")
+    assert "pool 320 slots" in bench.workload_name("decode", False, 0, 256)
+    assert "1 sequence of 32768 tokens" in bench.workload_name("prefill", True, 32768)
+    name = bench.workload_name("prefill", False, 192, lengths=[64, 128])
+    assert "2 sequences of lengths [64, 128] (T=192)" in name and "pool 3 slots" in name
+    both = bench.workload_name("both", False, 38632)
+    assert "16 seqs" in both and "B=4096" in both
