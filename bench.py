@@ -17,6 +17,10 @@ under "spec_decode".  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
 
+Other workloads, each timed on its own: --part prefill with --prefill-workload
+long (one 32,768-token sequence) or --prefill-lengths L1,L2,..; --part decode
+with --decode-batch B and --spec-batch B (small batches).
+
 The traffic records under profiles/ (HBM bytes counted by rocprofv3) are
 written by ``--traffic-record``, from counter runs of this script.
 """
@@ -294,7 +298,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--spec-steps", type=int, default=10,
                     help="after the timed steps, time this many multi-token verify decodes "
-                         "(1024 requests x 4 tokens, cache pitch 8; 0: skip)")
+                         "(--spec-batch requests x 4 tokens, cache pitch 8; 0: skip)")
     ap.add_argument("--fused-gate-steps", type=int, default=10,
                     help="after the timed steps, time this many passes through the fused-gate "
                          "entry points (0: skip)")
