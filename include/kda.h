@@ -135,7 +135,8 @@ size_t kda_chunk_prefill_workspace_size(const kda_prefill_desc *desc);
  *               pool mode: must be NULL or equal to `state`; the final state of
  *               sequence n is written to the same pool row it was read from.
  *               Rows not indexed are neither read nor written.  With several
- *               negative indices the sentinel row's content is unspecified.
+ *               negative indices the sentinel row's content, and the o rows of
+ *               those sequences, are unspecified.
  *   o           [T, hv, dv] io dtype; must not alias any input.
  *   workspace   device buffer of at least kda_chunk_prefill_workspace_size().
  * A sequence of length 0 writes no o rows and leaves its state unchanged
@@ -227,7 +228,9 @@ typedef struct {
  *   q, k  [B, hk, dk] io dtype;  v [B, hv, dv] io dtype
  *   g     [B, hv, dk] (CHANNEL) or [B, hv] (SCALAR) fp32;  beta [B, hv] fp32
  *   state_pool     [num_slots, hv, dv, dk] state dtype, read and written in place
- *   state_indices  [B] int32; an index < 0 selects slot num_slots - 1
+ *   state_indices  [B] int32; an index < 0 selects slot num_slots - 1 (with
+ *                  several negative indices the sentinel row's content, and
+ *                  the o of those requests, are unspecified)
  *   o     [B, hv, dv] io dtype
  * The launch grid is (hv x dv / tile, ceil(B / Z), Z) with Z = ceil(B / 65535):
  * head (with value tile) on x and the batch over y and z, so batch and head
@@ -303,7 +306,9 @@ typedef struct {
  *   g     [T, hv, dk] (CHANNEL) or [T, hv] (SCALAR) fp32;  beta [T, hv] fp32
  *   cu_seqlens     [N + 1] int32 (device)
  *   state_pool     [num_slots, hv, dv, dk] state dtype
- *   state_indices  [N] int32
+ *   state_indices  [N] int32 (with update_pool and several negative indices
+ *                  the sentinel row's content, and the o and cached steps of
+ *                  those requests, are unspecified)
  *   intermediate_states  [N, cache_pitch, hv, dv, dk] state dtype, or NULL
  *                  when cache_pitch is 0; steps at or beyond cache_pitch are
  *                  not cached; must not overlap any other argument
