@@ -107,6 +107,32 @@ def test_kimi_shaped_realistic_gates_full(K, oracle):
     assert torch.equal(pool[torch.as_tensor(untouched).cuda()].cpu(), pool_before[torch.as_tensor(untouched)])
 
 
+def test_long_prompt_full_call(K, oracle):
+    """The long-prompt workload: one sequence of 32,768 tokens, 32 heads,
+    K = V = 128, realistic gates, in pool mode as the bench calls it (32
+    chains of 512 chunk steps: the state kernel's four-part form).  The whole
+    call runs; every output of four heads and their final states are compared
+    with the oracle (heads do not interact), and the other pool row stays
+    untouched."""
+    say("generating long-prompt workload (1 x 32768 tokens, 32 heads)")
+    inp = W.long_prompt_32k()
+    S = inp.pool.shape[0]
+    slots = oracle.map_slot(inp.indices.numpy(), S)
+    sl = torch.as_tensor(slots)
+    pool_before = inp.pool.clone()
+    pool = dev(inp.pool)
+    o, _ = K.chunk_prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                           dev(inp.cu_seqlens), initial_state=pool, state_indices=dev(inp.indices))
+    torch.cuda.synchronize()
+    heads = [0, 9, 22, 31]
+    sel = lambda x: x[:, heads].contiguous()
+    o_ref, ht_ref = oracle.prefill(sel(inp.q), sel(inp.k), sel(inp.v), sel(inp.g), sel(inp.beta),
+                                   inp.cu_seqlens, h0=sel(pool_before[sl]))
+    check("long prompt, heads %s" % heads, o[:, heads], pool[sl.cuda()][:, heads], o_ref, ht_ref)
+    untouched = np.setdiff1d(np.arange(S), slots)
+    assert torch.equal(pool[torch.as_tensor(untouched).cuda()].cpu(), pool_before[torch.as_tensor(untouched)])
+
+
 @pytest.mark.parametrize("gate", ["moderate", "realistic"])
 def test_scalar_gate_gdn(K, oracle, gate):
     inp = W.make_prefill(61, [200, 64, 1, 77], 2, 4, 128, 128, gate=gate, scalar_gate=True, h0="random")
