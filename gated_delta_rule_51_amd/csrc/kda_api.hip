@@ -112,15 +112,17 @@ kda_status prefill_impl(const kda_prefill_desc *d, const void *q, const void *k,
     if (T == 0 && !final_state) return KDA_OK;
 
     // Grids, all 1-D: intra over (chunk slot, head) items; state over
-    // (sequence, head) chains, one workgroup per chain, or with at most 256
-    // chains one per column part (two, or four with at most 64 chains).
+    // (sequence, head) chains, one workgroup per chain, or one per column
+    // part (two, or four with at most 64 chains) with at most 256 chains or
+    // short sequences.
     int dev = 0, max_x = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_x, hipDeviceAttributeMaxGridDimX, dev) != hipSuccess)
         return KDA_ERR_HIP;
     const long slots = (T + 63L * N) / 64;
     const long intra_wgs = slots * d->hv;
-    const long state_wgs = (long)d->hv * N;   // one workgroup per (sequence, head) chain
+    // up to four column-part workgroups per (sequence, head) chain, in groups of eight chains
+    const long state_wgs = ((long)d->hv * N + 8) * 4;
     if (intra_wgs > max_x || state_wgs > max_x) return KDA_ERR_UNSUPPORTED;
 
     kda::PrefillArgs a{};

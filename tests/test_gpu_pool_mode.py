@@ -7,12 +7,13 @@
   untouched, and ``final_state is pool``;
 * the same recipe with one index set to -1 (the sentinel, last slot);
 * the same recipe through the fused-gate entry point (raw a and b);
-* more than 256 (sequence, head) chains, where the state kernel runs both
-  column parts of a chain in one sixteen-wave workgroup, with a bf16 pool and
-  with fp32 io;
-* 65 to 256 chains, where each column part is a workgroup of its own, with
-  the same two variants (the four-part form for at most 64 chains is covered
-  by the five-sequence recipes above).
+* more than 256 (sequence, head) chains of sequences longer than 1024 tokens
+  on average, where the state kernel runs both column parts of a chain in one
+  sixteen-wave workgroup, with a bf16 pool and with fp32 io;
+* 65 to 256 chains, and more than 256 chains of shorter sequences, where each
+  column part is a workgroup of its own, with the same two variants (the
+  four-part form for at most 64 chains is covered by the five-sequence
+  recipes above).
 
 Each pool-mode result is also held to the oracle's tolerances.
 """
@@ -93,18 +94,28 @@ def test_gdn_pool_mode_fused_gate(K, oracle):
 
 
 def test_many_chains_bf16_pool(K, oracle):
-    """40 sequences x 8 heads = 320 chains with V = 128 (sixteen-wave state
-    workgroups), bf16 pool of 48 slots with one -1 index."""
-    inp = W.make_prefill(81, (40, 1, 300), 4, 8, 128, 128, gate="realistic", pool_slots=48,
+    """40 sequences of 1100..1500 tokens x 8 heads = 320 chains with V = 128
+    (sixteen-wave state workgroups: more than 256 chains, sequences longer
+    than 1024 tokens on average), bf16 pool of 48 slots with one -1 index."""
+    inp = W.make_prefill(81, (40, 1100, 1500), 4, 8, 128, 128, gate="realistic", pool_slots=48,
                          state_dtype="bf16", pad_one=True)
     pool_vs_dense(K, oracle, inp, "320 chains, bf16 pool")
 
 
 def test_many_chains_fp32_io(K, oracle):
     """The same shape with fp32 q, k, v and o and an fp32 pool."""
-    inp = W.make_prefill(82, (40, 1, 300), 4, 8, 128, 128, io="f32", gate="realistic", pool_slots=48,
+    inp = W.make_prefill(82, (40, 1100, 1500), 4, 8, 128, 128, io="f32", gate="realistic", pool_slots=48,
                          pad_one=True, scale=128 ** -0.5)
     pool_vs_dense(K, oracle, inp, "320 chains, fp32 io")
+
+
+@pytest.mark.parametrize("io,state", [("bf16", "bf16"), ("f32", "f32")])
+def test_many_short_chains(K, oracle, io, state):
+    """40 sequences of 1..300 tokens x 8 heads = 320 chains with V = 128: with
+    short sequences a workgroup per 64-column part, as for few chains."""
+    inp = W.make_prefill(84, (40, 1, 300), 4, 8, 128, 128, io=io, gate="realistic", pool_slots=48,
+                         state_dtype=state, pad_one=True, scale=128 ** -0.5)
+    pool_vs_dense(K, oracle, inp, "320 short chains, %s io, %s pool" % (io, state))
 
 
 @pytest.mark.parametrize("io,state", [("bf16", "bf16"), ("f32", "f32")])
