@@ -142,6 +142,12 @@ size_t kda_chunk_prefill_workspace_size(const kda_prefill_desc *desc);
  * A sequence of length 0 writes no o rows and leaves its state unchanged
  * (copied to final_state in dense mode).  Pool mode and dense mode run the
  * same kernels with the same tiling and produce bit-identical o and states.
+ * Every chunk is processed as 64 tokens, so for pool-mode batches of very
+ * short sequences (at most about 8 tokens each) kda_recurrent_decode_multi
+ * with update_pool set and no step cache computes the same recurrence
+ * faster, in fp32 (MI355X, 32 heads, K = V = 128: 4096 sequences x 4 tokens
+ * 5.1 ms against 8.8 ms here; at 8 tokens they are even, and from 16 tokens
+ * this entry point is faster).
  */
 kda_status kda_chunk_prefill(const kda_prefill_desc *desc,
                              const void *q, const void *k, const void *v,
