@@ -88,6 +88,35 @@ def test_many_state_chains(K, oracle):
     run_and_check(K, oracle, inp, "1200 chains, V=128")
 
 
+def test_many_short_sequences_full_heads(K, oracle):
+    """1024 sequences of 32 tokens x 32 heads, K = V = 128, pool mode: 32,768
+    chains of one half-filled chunk each (a workgroup per column part, as for
+    short sequences; every length ties, so the order is the index order).
+    The whole call runs; two heads of every sequence are compared with the
+    oracle, and the unindexed pool row stays untouched."""
+    inp = W.make_prefill(78, [32] * 1024, 32, 32, 128, 128, gate="realistic", pool_slots=1026)
+    S = inp.pool.shape[0]
+    slots = oracle.map_slot(inp.indices.numpy(), S)
+    sl = torch.as_tensor(slots)
+    pool_before = inp.pool.clone()
+    pool = dev(inp.pool)
+    o, _ = K.chunk_prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(inp.cu_seqlens),
+                           initial_state=pool, state_indices=dev(inp.indices))
+    torch.cuda.synchronize()
+    heads = [5, 26]
+    sel = lambda x: x[:, heads].contiguous()
+    o_ref, ht_ref = oracle.prefill(sel(inp.q), sel(inp.k), sel(inp.v), sel(inp.g), sel(inp.beta),
+                                   inp.cu_seqlens, h0=sel(pool_before[sl]))
+    og = host(o[:, heads])
+    assert np.isfinite(og).all()
+    e_o = max_abs(og, o_ref)
+    say("1024 x 32 tokens, heads %s: o max-abs %.3e" % (heads, e_o))
+    assert e_o <= O_MAXABS
+    check_states("1024 x 32 tokens", host(pool[sl.cuda()][:, heads]), ht_ref)
+    untouched = np.setdiff1d(np.arange(S), slots)
+    assert torch.equal(pool[torch.as_tensor(untouched).cuda()].cpu(), pool_before[torch.as_tensor(untouched)])
+
+
 def test_large_token_count(K, oracle):
     """131,072 tokens (one sequence of 100,000) x 32 heads, K = V = 128: input
     tensors of 1 GB and a 4.5 GB workspace, so every byte offset past 2^32 is
