@@ -4,15 +4,16 @@ once the batch fills the chip.  A row's arithmetic does not depend on its
 tile, so the same requests give bit-identical outputs, states and cached
 steps on both sides of the switch.  Each test runs a batch just above the
 switch (whole-head tiles) and its first requests alone, just at it (32-row
-tiles), on copies of one pool, through the C ABI.  Both tile forms are also
-held to the oracle elsewhere: small batches in the decode and verify suites,
-the full-size workloads there too.
+tiles), on copies of one pool, through the C ABI.  The one-token decode's
+32-row tile result is also compared with the oracle here; both tile forms
+are held to it elsewhere too (small batches in the decode and verify suites,
+the full-size workloads there).
 """
 import pytest
 import torch
 
 import kda_workloads as W
-from gpu_util import dev, say
+from gpu_util import O_MAXABS, check_states, dev, host, max_abs, say
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +31,7 @@ def K():
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
-def test_decode_tile_switch(K, dk, dv):
+def test_decode_tile_switch(K, oracle, dk, dv):
     b_small = SMALL_ROWS_DECODE // (HV * dv)
     B = b_small + 8
     d = W.make_decode(800 + dk + dv, B, 8, HV, dk, dv, num_slots=B + 2, scale=dk ** -0.5)
@@ -45,6 +46,13 @@ def test_decode_tile_switch(K, dk, dv):
     rows = idx[:b_small].long()
     assert torch.equal(o_few, o_all[:b_small])
     assert torch.equal(pool_few[rows], pool_all[rows])
+    # the 32-row tile result against the oracle as well
+    o_ref, ht_ref = oracle.decode(d.q[:b_small], d.k[:b_small], d.v[:b_small], d.g[:b_small], d.beta[:b_small],
+                                  d.pool[d.indices[:b_small].long()], scale=d.scale)
+    e_o = max_abs(host(o_few), o_ref)
+    say("decode tile switch: o max-abs %.3e" % e_o)
+    assert e_o <= O_MAXABS
+    check_states("decode tile switch", host(pool_few[rows]), ht_ref)
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
