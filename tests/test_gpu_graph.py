@@ -63,6 +63,58 @@ def test_graph_replay_matches_eager(K):
         assert ok, r
 
 
+def test_graph_replay_verify_decode(K):
+    """The multi-token (verify) decode under capture: plain and fused-gate
+    calls with a per-step state cache, one updating its pool, replayed three
+    times with eager work between, each bit-identical to the eager calls."""
+    m = W.make_multi_decode(603, [4, 0, 3, 5, 1], 2, 4, 128, 128, num_slots=8, cache_pitch=4)
+    t = m.tok
+    T = {n: dev(getattr(t, n)) for n in ("q", "k", "v", "g", "beta", "cu_seqlens", "gx", "A_log", "dt_bias", "bx")}
+    idx = dev(m.indices)
+    pool0 = dev(m.pool)
+    pool = pool0.clone()
+    N = t.num_seqs
+    cache = torch.zeros(N, 4, 4, 128, 128, device="cuda")
+    cache_f = torch.zeros_like(cache)
+
+    def work():
+        o = K.recurrent_decode_multi(T["q"], T["k"], T["v"], T["g"], T["beta"], T["cu_seqlens"], pool, idx,
+                                     intermediate_states=cache, update_pool=True)
+        of = K.recurrent_decode_multi_fused_gate(T["q"], T["k"], T["v"], T["gx"], T["A_log"], T["dt_bias"],
+                                                 T["bx"], T["cu_seqlens"], pool0, idx,
+                                                 intermediate_states=cache_f, update_pool=False)
+        return o, of
+
+    o_e, of_e = (x.clone() for x in work())
+    pool_e, cache_e, cache_fe = pool.clone(), cache.clone(), cache_f.clone()
+    torch.cuda.synchronize()
+
+    pool.copy_(pool0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    pool.copy_(pool0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        o_g, of_g = work()
+    for r in range(3):
+        pool.copy_(pool0)
+        cache.zero_()
+        cache_f.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ok = (torch.equal(o_g, o_e) and torch.equal(of_g, of_e) and torch.equal(pool, pool_e)
+              and torch.equal(cache, cache_e) and torch.equal(cache_f, cache_fe))
+        say("verify graph replay %d: bit-identical %s (junk %.3f)" % (r, ok, float(junk)))
+        assert ok, r
+
+
 def test_graph_survives_workspace_growth(K):
     """A prefill captured on a stream keeps working after a larger eager
     prefill on that stream has replaced the stream's workspace: the replaced
